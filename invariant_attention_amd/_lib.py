@@ -1,0 +1,149 @@
+"""Thin ctypes binding of ``libbiattn.so`` (argument marshalling only).
+
+Every function here has the name of the C entry point it calls (``include/bi_attn.h``) and
+does nothing but turn torch tensors into pointers, sizes and the current HIP stream; all of
+the work runs in the library's HIP kernels. A non-OK status raises ``BiAttnError``. There is
+no fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbiattn.so")
+
+BI_F32, BI_BF16 = 0, 1
+BI_SPLIT_FIXED, BI_SPLIT_BY_BATCH = 0, 1
+BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
+
+EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode",
+            "bi_attn_prefill", "bi_status_string")
+
+
+class BiAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {bi_status_string(status)} (status {status})")
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("split_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("split_policy", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """Python mirror of ``bi_attn_cfg``."""
+
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int = 16
+    split_size: int = 256
+    dtype: int = BI_BF16
+    softmax_scale: float = 0.0
+    split_policy: int = BI_SPLIT_FIXED
+
+    def c(self) -> _Cfg:
+        return _Cfg(self.num_q_heads, self.num_kv_heads, self.head_dim, self.page_size,
+                    self.split_size, self.dtype, self.softmax_scale, self.split_policy)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == BI_BF16 else torch.float32
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    CP = ctypes.POINTER(_Cfg)
+    lib.bi_status_string.restype = ctypes.c_char_p
+    lib.bi_status_string.argtypes = [ctypes.c_int]
+    lib.bi_attn_workspace_bytes.restype = Z
+    lib.bi_attn_workspace_bytes.argtypes = [CP, I, I]
+    lib.bi_kv_page_update.restype = ctypes.c_int
+    lib.bi_kv_page_update.argtypes = [CP, P, P, P, P, P, I, I, I, I, P, P, P]
+    lib.bi_attn_decode.restype = ctypes.c_int
+    lib.bi_attn_decode.argtypes = [CP, P, P, P, P, I, I, P, I, I, P, P, Z, P]
+    lib.bi_attn_prefill.restype = ctypes.c_int
+    lib.bi_attn_prefill.argtypes = [CP, P, P, P, P, I, I, P, P, I, I, I, I, P, P, Z, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != BI_OK:
+        raise BiAttnError(status, where)
+
+
+def bi_status_string(status: int) -> str:
+    return load().bi_status_string(int(status)).decode()
+
+
+def bi_attn_workspace_bytes(cfg: AttnConfig, rows_tokens: int, max_seq_len: int) -> int:
+    return int(load().bi_attn_workspace_bytes(ctypes.byref(cfg.c()), int(rows_tokens), int(max_seq_len)))
+
+
+def bi_kv_page_update(cfg: AttnConfig, k_new: torch.Tensor, v_new: torch.Tensor,
+                      q_starts: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Write a step's new K/V rows into their pages (before attention, same stream)."""
+    st = load().bi_kv_page_update(
+        ctypes.byref(cfg.c()), _ptr(k_new), _ptr(v_new), _ptr(q_starts), _ptr(seq_lens),
+        _ptr(page_table), page_table.shape[1], k_cache.shape[0], seq_lens.shape[0],
+        k_new.shape[0], _ptr(k_cache), _ptr(v_cache), _stream(stream))
+    _check(st, "bi_kv_page_update")
+
+
+def bi_attn_decode(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                   out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """One query token per sequence; ``out`` fp32 ``[batch][Hq][D]``."""
+    st = load().bi_attn_decode(
+        ctypes.byref(cfg.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        page_table.shape[1], k_cache.shape[0], _ptr(seq_lens), seq_lens.shape[0],
+        int(max_seq_len), _ptr(out), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "bi_attn_decode")
+
+
+def bi_attn_prefill(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    page_table: torch.Tensor, q_starts: torch.Tensor, seq_lens: torch.Tensor,
+                    max_q_len: int, max_seq_len: int, out: torch.Tensor,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Chunked prefill of ``q [T][Hq][D]``; ``out`` fp32 ``[T][Hq][D]``."""
+    st = load().bi_attn_prefill(
+        ctypes.byref(cfg.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        page_table.shape[1], k_cache.shape[0], _ptr(q_starts), _ptr(seq_lens),
+        seq_lens.shape[0], q.shape[0], int(max_q_len), int(max_seq_len), _ptr(out),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "bi_attn_prefill")

@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports what include/bi_attn.h declares, and validates arguments.
+
+CPU only: every call below fails validation, so nothing is ever launched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_attention_amd as bi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bi_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bi.load()
+    names = declared_functions()
+    assert set(names) == set(bi.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert bi.bi_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert bi.bi_status_string(s) not in ("ok", "unknown status")
+    assert bi.bi_status_string(99) == "unknown status"
+
+
+BASE = dict(num_q_heads=64, num_kv_heads=4, head_dim=128, page_size=16, split_size=256,
+            dtype=bi.BI_BF16, softmax_scale=0.0, split_policy=bi.BI_SPLIT_FIXED)
+
+
+@pytest.mark.parametrize("override,status", [
+    (dict(num_q_heads=63), bi._lib.BI_EINVAL),                 # Hq % Hkv != 0
+    (dict(num_kv_heads=0), bi._lib.BI_EINVAL),
+    (dict(head_dim=96), bi._lib.BI_EUNSUPPORTED),
+    (dict(head_dim=256), bi._lib.BI_EUNSUPPORTED),
+    (dict(page_size=32), bi._lib.BI_EUNSUPPORTED),
+    (dict(split_size=48), bi._lib.BI_EUNSUPPORTED),            # not a multiple of 32
+    (dict(split_size=0), bi._lib.BI_EINVAL),
+    (dict(dtype=7), bi._lib.BI_EINVAL),
+    (dict(split_policy=3), bi._lib.BI_EINVAL),
+    (dict(softmax_scale=-1.0), bi._lib.BI_EINVAL),
+    (dict(softmax_scale=float("nan")), bi._lib.BI_EINVAL),
+    (dict(num_q_heads=12, num_kv_heads=4), bi._lib.BI_EUNSUPPORTED),   # group 3
+    (dict(num_q_heads=128, num_kv_heads=1), bi._lib.BI_EUNSUPPORTED),  # group 128
+])
+def test_config_validation(override, status):
+    cfg = bi.AttnConfig(**{**BASE, **override})
+    lib = bi.load()
+    c = cfg.c()
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.bi_attn_decode(ctypes.byref(c), fake, fake, fake, fake, 4, 4, fake, 1, 16, fake,
+                            fake, 1 << 30, None)
+    assert st == status
+    st = lib.bi_attn_prefill(ctypes.byref(c), fake, fake, fake, fake, 4, 4, fake, fake, 1, 1, 1,
+                             16, fake, None, 0, None)
+    assert st == status
+    st = lib.bi_kv_page_update(ctypes.byref(c), fake, fake, fake, fake, fake, 4, 4, 1, 1, fake,
+                               fake, None)
+    assert st == status
+    assert lib.bi_attn_workspace_bytes(ctypes.byref(c), 4, 100) == 0
+
+
+def test_argument_validation_launches_nothing():
+    lib = bi.load()
+    c = bi.AttnConfig(**BASE).c()
+    f = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    E = bi._lib
+    # null pointers
+    assert lib.bi_attn_decode(ctypes.byref(c), None, f, f, f, 4, 4, f, 1, 16, f, f, 1 << 30, None) == E.BI_EINVAL
+    assert lib.bi_attn_prefill(ctypes.byref(c), f, f, f, f, 4, 4, None, f, 1, 1, 1, 16, f, None, 0, None) == E.BI_EINVAL
+    assert lib.bi_kv_page_update(ctypes.byref(c), f, f, f, f, None, 4, 4, 1, 1, f, f, None) == E.BI_EINVAL
+    assert lib.bi_attn_decode(None, f, f, f, f, 4, 4, f, 1, 16, f, f, 1 << 30, None) == E.BI_EINVAL
+    # negative sizes
+    assert lib.bi_attn_decode(ctypes.byref(c), f, f, f, f, 4, 4, f, -1, 16, f, f, 1 << 30, None) == E.BI_EINVAL
+    assert lib.bi_attn_prefill(ctypes.byref(c), f, f, f, f, 4, 4, f, f, 1, -2, 1, 16, f, None, 0, None) == E.BI_EINVAL
+    # misaligned
+    assert lib.bi_attn_decode(ctypes.byref(c), odd, f, f, f, 4, 4, f, 1, 16, f, f, 1 << 30, None) == E.BI_EINVAL
+    # workspace missing or too small
+    need = lib.bi_attn_workspace_bytes(ctypes.byref(c), 1, 16)
+    assert need > 0
+    assert lib.bi_attn_decode(ctypes.byref(c), f, f, f, f, 4, 4, f, 1, 16, f, None, 0, None) == E.BI_EWORKSPACE
+    assert lib.bi_attn_decode(ctypes.byref(c), f, f, f, f, 4, 4, f, 1, 16, f, f, need - 1, None) == E.BI_EWORKSPACE
+    # empty work is a no-op success
+    assert lib.bi_attn_decode(ctypes.byref(c), None, None, None, None, 0, 0, None, 0, 0, None, None, 0, None) == E.BI_OK
+    assert lib.bi_attn_prefill(ctypes.byref(c), None, None, None, None, 0, 0, None, None, 0, 0, 0, 0, None, None, 0, None) == E.BI_OK
+
+
+def test_workspace_bytes_formula():
+    lib = bi.load()
+    c = bi.AttnConfig(**BASE).c()
+    # fixed policy: rows * ceil(len / S) * (8 + 4 D), with the (m, l) block padded to 256 B
+    for rows, L in ((1, 1), (3, 256), (64, 8192), (8, 131072)):
+        J = (L + 255) // 256
+        ml = (rows * 64 * J * 8 + 255) // 256 * 256
+        assert lib.bi_attn_workspace_bytes(ctypes.byref(c), rows, L) == ml + rows * 64 * J * 128 * 4
