@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant paged attention path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input: the page update of
+the step's new tokens, then attention. The headline workload is the bf16 decode sweep at its
+largest batch (64 sequences, 32 query heads, 4 KV heads, head_dim 128, context lengths
+U[128, 8192], 16-token pages in a shuffled pool, fixed split size 256); ``value`` is its
+algorithmic HBM GB/s. The chunked-prefill workload (16 sequences, 64/4 heads, cached prefix
+U[0, 16384], new chunk U[1, 2048]) is measured in the same run and reported under
+``prefill`` in TFLOP/s. Every figure counts only because the same run checks parity against
+the fp64 oracle and bitwise batch invariance first.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import invariant_attention_amd as bi  # noqa: E402
+from synth import CONFIG_SHAPES, SeqSpec, build_batch  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+METRIC = "decode attn HBM GB/s + prefill attn TFLOP/s at bitwise batch invariance"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def dev(x, dt):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dt)
+
+
+def cfg_of(shape, policy=bi.BI_SPLIT_FIXED):
+    return bi.AttnConfig(shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.page_size,
+                         shape.split_size, bi.BI_BF16, 0.0, policy)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every call below is launched on)."""
+
+    def __init__(self, n):
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def mark(self, i):
+        self.ev[i].record()
+
+    def ms(self, i, j):
+        return self.ev[i].elapsed_time(self.ev[j])
+
+
+# ----------------------------------------------------------------------------- decode
+def decode_workload(seed=2026, batch=64):
+    shape = CONFIG_SHAPES["decode_bf16"]
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(128, 8193, batch)]
+    seqs = [SeqSpec(i, L - 1, 1) for i, L in enumerate(lens)]
+    return shape, build_batch(shape, seqs, seed=seed, page_seed=seed + 1)
+
+
+def decode_bytes(shape, lens):
+    """Algorithmic bytes of one decode step: K and V once, q in, fp32 out, the page table."""
+    D, Hq, Hkv = shape.head_dim, shape.num_q_heads, shape.num_kv_heads
+    lens = np.asarray(lens, np.int64)
+    kv = int((lens * Hkv * D * 2 * 2).sum())
+    pages = int(((lens + 15) // 16).sum()) * 4
+    q_in = len(lens) * Hq * D * 2
+    out = len(lens) * Hq * D * 4
+    return dict(total=kv + pages + q_in + out, split_kernel=kv + pages + q_in, kv=kv)
+
+
+def run_decode_bench(args, result):
+    shape, bt = decode_workload()
+    cfg = cfg_of(shape)
+    B = bt.batch
+    log(f"decode workload: B={B}, KV {decode_bytes(shape, bt.seq_lens)['kv'] / 1e6:.0f} MB")
+    q, kn, vn = (dev(bt.q, torch.bfloat16), dev(bt.k_new, torch.bfloat16), dev(bt.v_new, torch.bfloat16))
+    pt, sl = dev(bt.page_table, torch.int32), dev(bt.seq_lens, torch.int32)
+    qs = dev(bt.q_starts, torch.int32)
+    mx = bt.max_seq_len
+    # R copies of the pool so no step finds its KV in the 256 MB last-level cache
+    R = args.rotate
+    pools = [(dev(bt.k_pool, torch.bfloat16), dev(bt.v_pool, torch.bfloat16)) for _ in range(R)]
+    ws = torch.empty(bi.bi_attn_workspace_bytes(cfg, B, mx) // 4 + 64, device="cuda")
+    out = torch.empty((B, shape.num_q_heads, shape.head_dim), device="cuda")
+    for kc, vc in pools:
+        bi.bi_kv_page_update(cfg, kn, vn, qs, sl, pt, kc, vc)
+
+    # --- parity and invariance, in this run, before any timing
+    bi.bi_attn_decode(cfg, q, pools[0][0], pools[0][1], pt, sl, mx, out, ws)
+    ref_bits = out.clone()
+    for p in (0, 17, 63):
+        it = torch.tensor([p], device="cuda", dtype=torch.long)
+        o1 = torch.empty((1, shape.num_q_heads, shape.head_dim), device="cuda")
+        bi.bi_attn_decode(cfg, q[it].contiguous(), pools[0][0], pools[0][1], pt[it].contiguous(),
+                          sl[it].contiguous(), mx, o1, ws)
+        assert torch.equal(o1.view(torch.int32), ref_bits[p:p + 1].view(torch.int32)), \
+            f"decode invariance broken for sequence {p} (B=1 vs B={B})"
+    # the same batch in reversed order: every row's bits unchanged
+    rev = torch.arange(B - 1, -1, -1, device="cuda")
+    o_rev = torch.empty_like(out)
+    bi.bi_attn_decode(cfg, q[rev].contiguous(), pools[1 % R][0], pools[1 % R][1],
+                      pt[rev].contiguous(), sl[rev].contiguous(), mx, o_rev, ws)
+    assert torch.equal(o_rev[rev].view(torch.int32), ref_bits.view(torch.int32)), "order invariance"
+    result["invariance"] = {"decode": "bitwise: B=1 vs B=64 for sequences 0, 17, 63; "
+                                      "reversed batch order; all rows equal"}
+    gpu_out = ref_bits.cpu().double().numpy()
+
+    # --- the non-invariant comparison variant (split count chosen by batch)
+    cfg_v = cfg_of(shape, bi.BI_SPLIT_BY_BATCH)
+    ws_v = torch.empty(bi.bi_attn_workspace_bytes(cfg_v, B, mx) // 4 + 64, device="cuda")
+
+    def step(i, c, w, tm=None):
+        kc, vc = pools[i % R]
+        if tm: tm.mark(0)
+        bi.bi_kv_page_update(c, kn, vn, qs, sl, pt, kc, vc)
+        if tm: tm.mark(1)
+        bi.bi_attn_decode_partials(c, q, kc, vc, pt, sl, mx, w)
+        if tm: tm.mark(2)
+        bi.bi_attn_decode_combine(c, sl, mx, out, w)
+        if tm: tm.mark(3)
+
+    for i in range(args.warmup):
+        step(i, cfg, ws)
+    timers = [Timer(4) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, cfg, ws, timers[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    pu = np.mean([t.ms(0, 1) for t in timers])
+    part = np.mean([t.ms(1, 2) for t in timers])
+    comb = np.mean([t.ms(2, 3) for t in timers])
+    gpu_step = np.mean([t.ms(0, 3) for t in timers])
+
+    # variant timing (same step shape)
+    for i in range(args.warmup):
+        step(i, cfg_v, ws_v)
+    timers_v = [Timer(4) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, cfg_v, ws_v, timers_v[i])
+    torch.cuda.synchronize()
+    var_step = np.mean([t.ms(0, 3) for t in timers_v])
+
+    nb = decode_bytes(shape, bt.seq_lens)
+    step_ms = max(wall * 1e3, gpu_step)
+    result.update(
+        value=nb["total"] / (step_ms * 1e-3) / 1e9,
+        ms_per_step=step_ms,
+        config={"workload": "decode_bf16: batch 64, 1 query token each, Hq 32, Hkv 4, D 128, "
+                            "context U[128,8192], page 16 (shuffled), split 256",
+                "global_batch": B, "seq_len": int(np.mean(bt.seq_lens)), "parallelism": "none"},
+    )
+    split_gbs = nb["split_kernel"] / (part * 1e-3) / 1e9
+    result["roofline"] = {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1>",
+                          "achieved": split_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": split_gbs / HBM_PEAK_GBS, "traffic": None,
+                          "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": part}
+    result["decode_breakdown_ms"] = {"page_update": pu, "partials": part, "combine": comb,
+                                     "step_events": gpu_step, "step_wall": wall * 1e3}
+    result["variant_slowdown"] = {"decode": gpu_step / var_step - 1.0,
+                                  "decode_ms": {"invariant": gpu_step, "split_by_batch": var_step}}
+
+    # --- sweep over batch sizes (first B sequences of the same workload)
+    sweep = []
+    for Bs in (1, 2, 4, 8, 16, 32, 64):
+        idx = torch.arange(Bs, device="cuda")
+        qb, ptb, slb = q[idx].contiguous(), pt[idx].contiguous(), sl[idx].contiguous()
+        ob = torch.empty((Bs, shape.num_q_heads, shape.head_dim), device="cuda")
+        mxb = int(bt.seq_lens[:Bs].max())
+        n = max(args.steps, 20)
+        for i in range(5):
+            bi.bi_attn_decode(cfg, qb, pools[i % R][0], pools[i % R][1], ptb, slb, mxb, ob, ws)
+        tm = Timer(2)
+        torch.cuda.synchronize()
+        tm.mark(0)
+        for i in range(n):
+            bi.bi_attn_decode(cfg, qb, pools[i % R][0], pools[i % R][1], ptb, slb, mxb, ob, ws)
+        tm.mark(1)
+        torch.cuda.synchronize()
+        ms = tm.ms(0, 1) / n
+        byt = decode_bytes(shape, bt.seq_lens[:Bs])["total"]
+        sweep.append({"batch": Bs, "us": ms * 1e3, "GBps": byt / (ms * 1e-3) / 1e9})
+    result["decode_sweep"] = sweep
+    return bt, gpu_out
+
+
+# ----------------------------------------------------------------------------- prefill
+def prefill_workload(seed=2027):
+    shape = CONFIG_SHAPES["prefill_bf16"]
+    rng = np.random.default_rng(seed)
+    specs = [SeqSpec(i, int(rng.integers(0, 16385)), int(rng.integers(1, 2049))) for i in range(16)]
+    return shape, build_batch(shape, specs, seed=seed, page_seed=seed + 1)
+
+
+def prefill_flops(bt):
+    D, Hq = bt.shape.head_dim, bt.shape.num_q_heads
+    tot = 0
+    for s in bt.seqs:
+        n = s.n_new
+        tot += 4 * D * Hq * (n * (s.cached + 1) + n * (n - 1) // 2)
+    return tot
+
+
+def run_prefill_bench(args, result):
+    shape, bt = prefill_workload()
+    cfg = cfg_of(shape)
+    log(f"prefill workload: {bt.total_tokens} new tokens, {prefill_flops(bt) / 1e12:.2f} TFLOP")
+    q, kn, vn = (dev(bt.q, torch.bfloat16), dev(bt.k_new, torch.bfloat16), dev(bt.v_new, torch.bfloat16))
+    kc, vc = dev(bt.k_pool, torch.bfloat16), dev(bt.v_pool, torch.bfloat16)
+    pt, sl, qs = dev(bt.page_table, torch.int32), dev(bt.seq_lens, torch.int32), dev(bt.q_starts, torch.int32)
+    out = torch.empty((bt.total_tokens, shape.num_q_heads, shape.head_dim), device="cuda")
+    bi.bi_kv_page_update(cfg, kn, vn, qs, sl, pt, kc, vc)
+    bi.bi_attn_prefill(cfg, q, kc, vc, pt, qs, sl, bt.max_q_len, bt.max_seq_len, out)
+    ref = out.clone()
+    # invariance: last token of every sequence through decode must match bitwise
+    last = torch.tensor([int(bt.q_starts[b + 1]) - 1 for b in range(bt.batch)], device="cuda")
+    od = torch.empty((bt.batch, shape.num_q_heads, shape.head_dim), device="cuda")
+    ws = torch.empty(bi.bi_attn_workspace_bytes(cfg, bt.batch, bt.max_seq_len) // 4 + 64, device="cuda")
+    bi.bi_attn_decode(cfg, q[last].contiguous(), kc, vc, pt, sl, bt.max_seq_len, od, ws)
+    assert torch.equal(od.view(torch.int32), ref[last].view(torch.int32)), "prefill vs decode bits"
+    result.setdefault("invariance", {})["prefill"] = ("bitwise: last token of each of the 16 "
+                                                      "sequences, prefill vs decode")
+
+    def run(c, n, warm):
+        for _ in range(warm):
+            bi.bi_attn_prefill(c, q, kc, vc, pt, qs, sl, bt.max_q_len, bt.max_seq_len, out)
+        tms = [Timer(3) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            tms[i].mark(0)
+            bi.bi_kv_page_update(c, kn, vn, qs, sl, pt, kc, vc)
+            tms[i].mark(1)
+            bi.bi_attn_prefill(c, q, kc, vc, pt, qs, sl, bt.max_q_len, bt.max_seq_len, out)
+            tms[i].mark(2)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n * 1e3
+        return (np.mean([t.ms(1, 2) for t in tms]), np.mean([t.ms(0, 2) for t in tms]), wall)
+
+    n = max(3, args.steps // 5)
+    kern, step_ms, wall = run(cfg, n, max(1, args.warmup // 5))
+    kern_v, step_v, _ = run(cfg_of(shape, bi.BI_SPLIT_BY_BATCH), n, 1)
+    fl = prefill_flops(bt)
+    tf = fl / (kern * 1e-3) / 1e12
+    result["prefill"] = {
+        "value": fl / (max(step_ms, wall) * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "kernel_tflops": tf, "ms_per_step": max(step_ms, wall), "kernel_ms": kern,
+        "flops_per_step": fl,
+        "config": {"workload": "prefill_bf16: 16 sequences, Hq 64, Hkv 4, D 128, cached prefix "
+                               "U[0,16384], chunk U[1,2048], page 16, split 256",
+                   "new_tokens": bt.total_tokens},
+    }
+    result["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel<bf16,128,2>",
+                                  "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}
+    result["variant_slowdown"]["prefill"] = kern / kern_v - 1.0
+    result["variant_slowdown"]["prefill_ms"] = {"invariant": kern, "split_by_batch": kern_v}
+    return bt, ref
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(result, bt_dec, gpu_dec, samples):
+    """Time the fp64 oracle on the host and use its outputs for the parity check."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    kc, vc = bt_dec.k_pool.copy(), bt_dec.v_pool.copy()
+    oracle.kv_page_update(bt_dec.k_new, bt_dec.v_new, bt_dec.q_starts, bt_dec.seq_lens,
+                          bt_dec.page_table, kc, vc)
+    n = min(samples, bt_dec.batch)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        ref = oracle.paged_attention(bt_dec.q[:n], kc, vc, bt_dec.page_table[:n],
+                                     bt_dec.q_starts[: n + 1], bt_dec.seq_lens[:n],
+                                     bt_dec.shape.num_kv_heads)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 5:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    byt = decode_bytes(bt_dec.shape, bt_dec.seq_lens[:n])["total"]
+    err = np.abs(gpu_dec[:n] - ref)
+    parity = {"decode_rows": int(n * bt_dec.shape.num_q_heads), "max_abs": float(err.max()),
+              "mean_abs": float(err.mean())}
+    assert err.max() <= 2e-3 and err.mean() <= 2e-4, parity
+    result["parity"] = parity
+    result["cpu_baseline"] = {"value": byt / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+                              "kind": "oracle",
+                              "sample": f"decode_bf16, first {n} of 64 sequences (all 32 heads), "
+                                        f"fp64 numpy, {reps} rep(s), {dt:.2f} s each",
+                              "host": platform.processor() or platform.machine(),
+                              "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-samples", type=int, default=64)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path is built and timed on a single device "
+              "(see the sharding paragraph of DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    bi.load()
+    torch.cuda.set_device(0)
+    result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded N(0,1), bf16-rounded; no model weights)"}
+    bt_dec, gpu_dec = run_decode_bench(args, result)
+    log(f"decode: {result['value']:.0f} GB/s per step, split kernel "
+        f"{result['roofline']['achieved']:.0f} GB/s")
+    if not args.no_prefill:
+        run_prefill_bench(args, result)
+        log(f"prefill: {result['prefill']['kernel_tflops']:.1f} TFLOP/s (kernel)")
+    if not args.no_cpu_baseline:
+        cpu_baseline(result, bt_dec, gpu_dec, args.cpu_samples)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

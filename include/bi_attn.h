@@ -123,6 +123,25 @@ int bi_attn_decode(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
                    hipStream_t stream);
 
 /*
+ * The two phases of bi_attn_decode, for callers that move or inspect the split partials
+ * between them (a context-parallel decode gathers partials from several devices and folds
+ * them in ascending split order on the row's owner), and for per-kernel timing.
+ * bi_attn_decode(...) == bi_attn_decode_partials(...) then bi_attn_decode_combine(...) on
+ * the same stream, with the same cfg, seq_lens, batch, max_seq_len and workspace, bit for bit.
+ * Partials layout in the workspace (fp32): first (m, l) pairs [batch*Hq][Jmax], padded to
+ * 256 bytes, then accumulators [batch*Hq][Jmax][D]; Jmax = ceil(max_seq_len / S) for
+ * BI_SPLIT_FIXED. m is in base-2 units (max of q.k * scale * log2(e)).
+ */
+int bi_attn_decode_partials(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* page_table, int32_t max_pages,
+                            int32_t num_pages, const int32_t* seq_lens, int32_t batch,
+                            int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+int bi_attn_decode_combine(const bi_attn_cfg* cfg, const int32_t* seq_lens, int32_t batch,
+                           int32_t max_seq_len, float* out, const void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Chunked prefill: n_new[b] = q_starts[b+1] - q_starts[b] new tokens per sequence (any
  * number, including 0 and 1), on top of a cached prefix; q [total_tokens][Hq][D]. Attention
  * reads all keys, prefix and chunk, through the page table (liuwei.blog post, section

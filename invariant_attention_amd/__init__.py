@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     bi_attn_decode,
+    bi_attn_decode_combine,
+    bi_attn_decode_partials,
     bi_attn_prefill,
     bi_attn_workspace_bytes,
     bi_kv_page_update,

@@ -23,7 +23,8 @@ BI_SPLIT_FIXED, BI_SPLIT_BY_BATCH = 0, 1
 BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode",
-            "bi_attn_prefill", "bi_status_string")
+            "bi_attn_decode_partials", "bi_attn_decode_combine", "bi_attn_prefill",
+            "bi_status_string")
 
 
 class BiAttnError(RuntimeError):
@@ -83,6 +84,10 @@ def load() -> ctypes.CDLL:
     lib.bi_kv_page_update.argtypes = [CP, P, P, P, P, P, I, I, I, I, P, P, P]
     lib.bi_attn_decode.restype = ctypes.c_int
     lib.bi_attn_decode.argtypes = [CP, P, P, P, P, I, I, P, I, I, P, P, Z, P]
+    lib.bi_attn_decode_partials.restype = ctypes.c_int
+    lib.bi_attn_decode_partials.argtypes = [CP, P, P, P, P, I, I, P, I, I, P, Z, P]
+    lib.bi_attn_decode_combine.restype = ctypes.c_int
+    lib.bi_attn_decode_combine.argtypes = [CP, P, I, I, P, P, Z, P]
     lib.bi_attn_prefill.restype = ctypes.c_int
     lib.bi_attn_prefill.argtypes = [CP, P, P, P, P, I, I, P, P, I, I, I, I, P, P, Z, P]
     _lib = lib
@@ -133,6 +138,31 @@ def bi_attn_decode(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_ca
         int(max_seq_len), _ptr(out), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "bi_attn_decode")
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def bi_attn_decode_partials(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, page_table: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, workspace: torch.Tensor,
+                            stream=None) -> None:
+    """First phase of decode: split partials into ``workspace``."""
+    st = load().bi_attn_decode_partials(
+        ctypes.byref(cfg.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        page_table.shape[1], k_cache.shape[0], _ptr(seq_lens), seq_lens.shape[0],
+        int(max_seq_len), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "bi_attn_decode_partials")
+
+
+def bi_attn_decode_combine(cfg: AttnConfig, seq_lens: torch.Tensor, max_seq_len: int,
+                           out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """Second phase of decode: ascending fold of the partials into ``out``."""
+    st = load().bi_attn_decode_combine(
+        ctypes.byref(cfg.c()), _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(out),
+        _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "bi_attn_decode_combine")
 
 
 def bi_attn_prefill(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -62,11 +62,16 @@ __device__ __forceinline__ const char* kv_row(const char* cache, const AttnParam
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode: one wave per split. Operands stream from HBM straight into MFMA registers.
+// Decode: one wave per split. Operands stream from HBM straight into MFMA registers, two
+// sub-tiles in flight: the loads of sub-tile t+1 are issued before sub-tile t is computed.
 template <typename E, int D, int NB>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(AttnParams a) {
+__global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void decode_split_kernel(AttnParams a) {
   using F = Frag<E, D>;
+  using KOp = typename F::KOp;
+  using VRow = typename F::VRow;
+  constexpr int NKS = F::NKS;
   constexpr int NM = D / 16;
+  constexpr int ROWB = F::ROWB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -78,43 +83,80 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(AttnParams a) {
   const int k_begin = j * S;
   if (k_begin > pos || j >= a.jmax) return;
   const int k_end = min(k_begin + S, pos + 1);
+  const int nsub = (k_end - k_begin + kSubTile - 1) / kSubTile;
+  const size_t head_stride = (size_t)kPage * ROWB;
+  const size_t page_stride = (size_t)a.hkv * head_stride;
+  const char* kbase = a.k_cache + kvh * head_stride;
+  const char* vbase = a.v_cache + kvh * head_stride;
+
+  // physical pages of the split, one logical page per lane, 64 at a time
+  const int lp0 = k_begin / kPage;
+  int pg = page_of(a, b, lp0 + lane, seq_len);
 
   typename F::Q qf[NB];
   RowState<D> st[NB];
+  int posv[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
+    posv[cb] = pos;
     const int hl = cb * 16 + c;   // head within the group
     if (hl < a.group) {
-      const char* row = a.q + ((size_t)b * a.hq + kvh * a.group + hl) * (size_t)(D * sizeof(E));
+      const char* row = a.q + ((size_t)b * a.hq + kvh * a.group + hl) * (size_t)ROWB;
       F::load_q(qf[cb], row, g);
     } else {
       F::zero_q(qf[cb]);
     }
   }
-  for (int key0 = k_begin; key0 < k_end; key0 += kSubTile) {
-    typename F::K kf;
-    typename F::VRaw vr;
+
+  struct Buf {
+    KOp k[2][NKS];
+    VRow v[8];
+  };
+  auto fetch = [&](Buf& buf, int t) {
+    if (t > 0 && (t & 31) == 0) pg = page_of(a, b, lp0 + 2 * t + lane, seq_len);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int page = page_of(a, b, (key0 >> 4) + kb, seq_len);
-      if (page >= 0) F::load_k_block(kf, kb, kv_row<E, D>(a.k_cache, a, page, kvh, c), g);
-      else F::zero_k_block(kf, kb);
-    }
+      const int page = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
+      if (page >= 0) {
+        const char* kp = kbase + (size_t)page * page_stride;
+        const char* vp = vbase + (size_t)page * page_stride;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = key0 + F::vkey(i, g);
-      const int page = page_of(a, b, key >> 4, seq_len);
-      if (page >= 0 && key < seq_len) F::load_v_key(vr, i, kv_row<E, D>(a.v_cache, a, page, kvh, key & 15), c);
-      else F::zero_v_key(vr, i);
-    }
-    typename F::V vf;
-    F::pack_v(vf, vr);
-    const bool first = key0 == k_begin;
-    const bool mask = key0 + kSubTile - 1 > pos;
+        for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
-      subtile_step<E, D>(st[cb], qf[cb], kf, vf, a.cscale, key0, g, pos, true, first, mask, false);
+        for (int i = 4 * kb; i < 4 * kb + 4; ++i)
+          buf.v[i] = F::v_row(vp + (F::vkey(i, g) - 16 * kb) * ROWB, c);
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::zero_k();
+#pragma unroll
+        for (int i = 4 * kb; i < 4 * kb + 4; ++i) buf.v[i] = F::zero_v();
+      }
+    }
+  };
+  auto compute = [&](Buf& buf, int t) {
+    const int key0 = k_begin + kSubTile * t;
+    if (key0 + kSubTile > seq_len) {
+      // stale slots past the sequence end: V rows become zero, scores are masked below
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (key0 + F::vkey(i, g) >= seq_len) buf.v[i] = F::zero_v();
+    }
+    auto getK = [&](int kb, int s2) { return buf.k[kb][s2]; };
+    auto getV = [&](int i, int part) { return F::v_pair(buf.v[i], part); };
+    subtile_step<E, D, NB, false>(st, qf, posv, getK, getV, a.cscale, key0, g, t == 0,
+                                  key0 + kSubTile - 1 > pos);
+  };
+
+  Buf b0, b1;
+  fetch(b0, 0);
+  for (int t = 0; t < nsub; t += 2) {
+    if (t + 1 < nsub) fetch(b1, t + 1);
+    compute(b0, t);
+    if (t + 1 >= nsub) break;
+    if (t + 2 < nsub) fetch(b0, t + 2);
+    compute(b1, t + 1);
   }
+
   // Partial of split j for every real head of the block.
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
@@ -185,23 +227,31 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
 
 // ------------------------------------------------------------------------------------------
 // Prefill: a workgroup owns a tile of query columns (token-major: column = token * G + head)
-// of one (sequence, KV head) and walks every split that any of its rows needs. K/V sub-tiles
-// are staged once in LDS and shared by the four waves; each wave holds NBW column blocks.
+// of one (sequence, KV head) and walks every 32-key sub-tile that any of its rows needs, in
+// ascending order, folding each finished split into the row state. K/V sub-tiles are staged
+// in LDS and shared by all NW waves (the global loads of sub-tile u+1 are in flight while u
+// is computed); each wave holds NBW column blocks. The row accumulator A, touched only when
+// a split ends, lives in LDS next to the sequence's cached page ids.
 template <int D, typename E> struct Lds {
   static constexpr int ROWB = D * (int)sizeof(E);
   static constexpr int STRIDE = ROWB + 16;              // pad rows against bank conflicts
-  static constexpr int BYTES = 2 * kSubTile * STRIDE;   // K then V
+  static constexpr int TILE = kSubTile * STRIDE;        // one K or V sub-tile
 };
+constexpr int kPageCache = 2048;
 
-template <typename E, int D, int NBW>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(AttnParams a) {
+template <typename E, int D, int NBW, int NW, bool LANESEL>
+__global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
   using F = Frag<E, D>;
   using LD = Lds<D, E>;
   constexpr int NM = D / 16;
-  constexpr int COLS = kWaves * NBW * 16;
-  __shared__ __attribute__((aligned(16))) char lds[LD::BYTES];
-  char* lds_k = lds;
-  char* lds_v = lds + kSubTile * LD::STRIDE;
+  constexpr int NT = 64 * NW;
+  constexpr int COLS = NW * NBW * 16;
+  constexpr int CHUNKS = LD::ROWB / 16;                  // 16-byte chunks per row
+  constexpr int TOTAL = 2 * kSubTile * CHUNKS;           // K and V chunks per sub-tile
+  constexpr int PER = (TOTAL + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) char lds_kv[2][LD::TILE];
+  __shared__ f32x4 lds_A[NW][NBW][NM][64];               // [wave][block][float4 e][lane]
+  __shared__ int lds_pages[kPageCache];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -210,21 +260,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(AttnParams a) {
   const int tq = COLS / G;                       // tokens per tile (G divides COLS)
   const int q0 = a.q_starts[b], q1 = a.q_starts[b + 1];
   const int n_new = q1 - q0;
-  const int t0 = blockIdx.x * tq;
-  if (t0 >= n_new || q1 > a.total_tokens || q0 < 0) return;
+  const int n_tiles = (n_new + tq - 1) / tq;
+  const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;   // later (longer) tiles first
+  if (tile >= n_tiles || q1 > a.total_tokens || q0 < 0) return;
+  const int t0 = tile * tq;
   const int seq_len = a.seq_lens[b];
   const bool bad_seq = seq_len > a.max_seq_len || n_new > seq_len;
   const int first_pos = seq_len - n_new;
   const int t_last = min(t0 + tq, n_new) - 1;
   const int pos_max_wg = first_pos + t_last;
   const int S = split_len(a, seq_len);
+  const size_t head_stride = (size_t)kPage * LD::ROWB;
+  const size_t page_stride = (size_t)a.hkv * head_stride;
 
   typename F::Q qf[NBW];
   RowState<D> st[NBW];
   float Mrow[NBW], Lrow[NBW];
-  f32x4 Arow[NBW][NM];
-  int pos_c[NBW], blk_min[NBW], blk_max[NBW];
+  int pos_c[NBW], blk_max[NBW];
   bool valid_c[NBW];
+  int wave_min = 0x7fffffff, wave_max = -1;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
     const int col0 = (wave * NBW + cb) * 16;
@@ -232,87 +286,120 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(AttnParams a) {
     const int tok = t0 + col / G;
     valid_c[cb] = tok < n_new && !bad_seq;
     pos_c[cb] = valid_c[cb] ? first_pos + tok : -1;
-    // block-wide position range of valid columns (wave-uniform)
     const int tok_lo = t0 + col0 / G, tok_hi = min(t0 + (col0 + 15) / G, n_new - 1);
-    blk_min[cb] = (tok_lo < n_new && !bad_seq) ? first_pos + tok_lo : 0x7fffffff;
     blk_max[cb] = (tok_lo < n_new && !bad_seq) ? first_pos + tok_hi : -1;
+    if (tok_lo < n_new && !bad_seq) {
+      wave_min = min(wave_min, first_pos + tok_lo);
+      wave_max = max(wave_max, first_pos + tok_hi);
+    }
     if (valid_c[cb]) {
-      const char* row = a.q + ((size_t)(q0 + tok) * a.hq + kvh * G + col % G) * (size_t)(D * sizeof(E));
+      const char* row = a.q + ((size_t)(q0 + tok) * a.hq + kvh * G + col % G) * (size_t)LD::ROWB;
       F::load_q(qf[cb], row, g);
     } else {
       F::zero_q(qf[cb]);
     }
     Mrow[cb] = 0.f;
     Lrow[cb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < NM; ++mb) Arow[cb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  int wave_max = -1;
-#pragma unroll
-  for (int cb = 0; cb < NBW; ++cb) wave_max = max(wave_max, blk_max[cb]);
 
-  const int n_splits = bad_seq ? 0 : pos_max_wg / S + 1;
-  for (int j = 0; j < n_splits; ++j) {
-    const int k_begin = j * S;
-    const int k_end = min(k_begin + S, pos_max_wg + 1);
-    for (int key0 = k_begin; key0 < k_end; key0 += kSubTile) {
-      __syncthreads();
-      // Stage K and V rows [key0, key0 + 32) in LDS; V rows at or past seq_len and rows of
-      // absent pages are zero, so no stale cache bytes reach an MFMA.
-      constexpr int CHUNKS = LD::ROWB / 16;               // 16-byte chunks per row
-      constexpr int TOTAL = 2 * kSubTile * CHUNKS;
-      for (int idx = threadIdx.x; idx < TOTAL; idx += kThreads) {
+  const int nsub = bad_seq ? 0 : (pos_max_wg + kSubTile) / kSubTile;
+  const int npg = min((nsub * kSubTile) / kPage, kPageCache);
+  for (int i = threadIdx.x; i < npg; i += NT) lds_pages[i] = page_of(a, b, i, seq_len);
+  __syncthreads();
+
+  u32x4 pre[PER];
+  auto stage_load = [&](int u) {
+    const int key0 = u * kSubTile;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = threadIdx.x + k * NT;
+      u32x4 val = {0, 0, 0, 0};
+      if (idx < TOTAL) {
         const int which = idx / (kSubTile * CHUNKS);       // 0 = K, 1 = V
         const int rem = idx - which * kSubTile * CHUNKS;
         const int r = rem / CHUNKS, ch = rem - r * CHUNKS;
         const int key = key0 + r;
-        const int page = page_of(a, b, key >> 4, seq_len);
-        u32x4 val = {0, 0, 0, 0};
+        const int lp = key / kPage;
+        const int page = lp < kPageCache ? lds_pages[lp] : page_of(a, b, lp, seq_len);
+        // V rows at or past seq_len and rows of absent pages stay zero, so no stale cache
+        // bytes reach an MFMA
         if (page >= 0 && (which == 0 || key < seq_len)) {
-          const char* src = kv_row<E, D>(which ? a.v_cache : a.k_cache, a, page, kvh, key & 15);
-          val = *(const u32x4*)(src + ch * 16);
+          const char* src = (which ? a.v_cache : a.k_cache) + (size_t)page * page_stride +
+                            kvh * head_stride + (key % kPage) * LD::ROWB + ch * 16;
+          val = *(const u32x4*)src;
         }
-        *(u32x4*)((which ? lds_v : lds_k) + r * LD::STRIDE + ch * 16) = val;
       }
-      __syncthreads();
-      if (wave_max < key0) continue;                      // no row of this wave sees these keys
-      typename F::K kf;
-      typename F::VRaw vr;
+      pre[k] = val;
+    }
+  };
+  auto stage_store = [&]() {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) F::load_k_block(kf, kb, lds_k + (16 * kb + c) * LD::STRIDE, g);
+    for (int k = 0; k < PER; ++k) {
+      const int idx = threadIdx.x + k * NT;
+      if (idx < TOTAL) {
+        const int which = idx / (kSubTile * CHUNKS);
+        const int rem = idx - which * kSubTile * CHUNKS;
+        const int r = rem / CHUNKS, ch = rem - r * CHUNKS;
+        *(u32x4*)(&lds_kv[which][r * LD::STRIDE + ch * 16]) = pre[k];
+      }
+    }
+  };
+
+  if (nsub > 0) stage_load(0);
+  for (int u = 0; u < nsub; ++u) {
+    const int key0 = u * kSubTile;
+    const int j = key0 / S;
+    const bool first = key0 == j * S;
+    const bool last_of_split = key0 + kSubTile == (j + 1) * S || u + 1 == nsub;
+    stage_store();
+    __syncthreads();
+    if (u + 1 < nsub) stage_load(u + 1);
+    if (wave_max >= key0) {
+      const char* kt = lds_kv[0];
+      const char* vt = lds_kv[1];
+      auto getK = [&](int kb, int s2) { return F::k_op(kt + (16 * kb + c) * LD::STRIDE, s2, g); };
+      auto getV = [&](int i, int part) { return F::v_pair_at(vt + F::vkey(i, g) * LD::STRIDE, c, part); };
+      if (key0 <= wave_min) {
+        // every valid row of the wave reaches key0: all blocks advance together
+        subtile_step<E, D, NBW, false>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
+                                       key0 + kSubTile - 1 > wave_min);
+      } else {
+        // some row stops before key0 (the diagonal of the tile): block by block, and row by
+        // row inside a block when a block holds several tokens (G < 16)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) F::load_v_key(vr, i, lds_v + F::vkey(i, g) * LD::STRIDE, c);
-      typename F::V vf;
-      F::pack_v(vf, vr);
-      const bool first = key0 == k_begin;
+        for (int cb = 0; cb < NBW; ++cb)
+          if (blk_max[cb] >= key0)
+            subtile_step<E, D, 1, LANESEL>(&st[cb], &qf[cb], &pos_c[cb], getK, getV, a.cscale,
+                                           key0, g, first, true);
+      }
+    }
+    if (last_of_split && wave_max >= j * S) {
+      // fold split j into every row whose position reaches it (also when this wave's rows
+      // ended before this last sub-tile of the split)
 #pragma unroll
       for (int cb = 0; cb < NBW; ++cb) {
-        if (blk_max[cb] < key0) continue;                 // whole block past its rows
-        // mask: some key lies past some valid row; partial: some valid row has not reached
-        // key0 and must keep its state (only when a block holds several tokens, G < 16).
-        const bool mask = key0 + kSubTile - 1 > blk_min[cb];
-        const bool partial = key0 > blk_min[cb];
-        subtile_step<E, D>(st[cb], qf[cb], kf, vf, a.cscale, key0, g, pos_c[cb],
-                           pos_c[cb] >= key0, first, mask, partial);
-      }
-    }
-    // Fold split j into every row whose position reaches it.
-#pragma unroll
-    for (int cb = 0; cb < NBW; ++cb) {
-      if (blk_max[cb] < k_begin) continue;
-      const bool act = pos_c[cb] >= k_begin;
-      float M = Mrow[cb], L = Lrow[cb], fa, fb;
-      fold_scalars(M, L, st[cb].m, st[cb].l, j == 0, fa, fb);
-      if (act) {
-        Mrow[cb] = M;
-        Lrow[cb] = L;
-#pragma unroll
-        for (int mb = 0; mb < NM; ++mb)
+        if (blk_max[cb] < j * S) continue;
+        const bool act = pos_c[cb] >= j * S;
+        float M = Mrow[cb], L = Lrow[cb], fa, fb;
+        fold_scalars(M, L, st[cb].m, st[cb].l, j == 0, fa, fb);
+        if (act) {
+          Mrow[cb] = M;
+          Lrow[cb] = L;
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            Arow[cb][mb][r] = fold_elem(Arow[cb][mb][r], st[cb].acc[mb][r], fa, fb, j == 0);
+#pragma unroll
+            for (int m4 = 0; m4 < NM / 4; ++m4) {
+              f32x4& slot = lds_A[wave][cb][r * (NM / 4) + m4][lane];
+              f32x4 A = j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                A[e] = fold_elem(A[e], st[cb].acc[4 * m4 + e][r], fa, fb, j == 0);
+              slot = A;
+            }
+        }
       }
     }
+    __syncthreads();
   }
   // Epilogue: out = A / L for every valid row.
 #pragma unroll
@@ -325,11 +412,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(AttnParams a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int mb = 0; mb < NM; mb += 4) {
+      for (int m4 = 0; m4 < NM / 4; ++m4) {
+        const f32x4 A = lds_A[wave][cb][r * (NM / 4) + m4][lane];
         f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = ok ? Arow[cb][mb + e][r] / Lrow[cb] : __builtin_nanf("");
-        *(f32x4*)(dst + r * NM + mb) = v;
+        for (int e = 0; e < 4; ++e) v[e] = ok ? A[e] / Lrow[cb] : __builtin_nanf("");
+        *(f32x4*)(dst + r * NM + 4 * m4) = v;
       }
   }
 }
@@ -452,25 +540,73 @@ AttnParams base_params(const bi_attn_cfg* c) {
 int launched() { return hipGetLastError() == hipSuccess ? BI_OK : BI_EHIP; }
 
 template <typename E, int D>
-int launch_decode(const AttnParams& a, hipStream_t s) {
+int launch_partials(const AttnParams& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.jmax + kWaves - 1) / kWaves), (unsigned)a.hkv, (unsigned)a.batch);
   if (a.group <= 16) hipLaunchKernelGGL((decode_split_kernel<E, D, 1>), grid, dim3(kThreads), 0, s, a);
   else if (a.group == 32) hipLaunchKernelGGL((decode_split_kernel<E, D, 2>), grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL((decode_split_kernel<E, D, 4>), grid, dim3(kThreads), 0, s, a);
-  if (launched() != BI_OK) return BI_EHIP;
-  const unsigned rows = (unsigned)((int64_t)a.batch * a.hq);
-  hipLaunchKernelGGL((combine_kernel<D>), dim3((rows + kWaves - 1) / kWaves), dim3(kThreads), 0, s, a);
   return launched();
+}
+
+int launch_combine(const AttnParams& a, int D, hipStream_t s) {
+  const unsigned rows = (unsigned)((int64_t)a.batch * a.hq);
+  const dim3 grid((rows + kWaves - 1) / kWaves);
+  if (D == 128) hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(kThreads), 0, s, a);
+  return launched();
+}
+
+// Validates a decode call and fills the parameters; BI_OK when there is work to launch.
+int decode_params(const bi_attn_cfg* cfg, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                  const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float* out,
+                  const void* workspace, size_t workspace_bytes, bool need_kv, bool need_out,
+                  AttnParams* a) {
+  int st = check_cfg(cfg);
+  if (st != BI_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || max_pages < 0 || num_pages < 0) return BI_EINVAL;
+  if (batch == 0) return -1;   // nothing to do
+  if (!seq_lens || max_seq_len == 0) return BI_EINVAL;
+  if (need_kv && (!q || !k_cache || !v_cache || !page_table || max_pages == 0 || num_pages == 0))
+    return BI_EINVAL;
+  if (need_kv && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))) return BI_EINVAL;
+  if (need_out && (!out || !aligned16(out))) return BI_EINVAL;
+  const size_t need = ws_bytes(cfg, batch, batch, max_seq_len);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return BI_EWORKSPACE;
+  *a = base_params(cfg);
+  a->q = (const char*)q;
+  a->k_cache = (const char*)k_cache;
+  a->v_cache = (const char*)v_cache;
+  a->page_table = page_table;
+  a->seq_lens = seq_lens;
+  a->out = out;
+  a->max_pages = max_pages;
+  a->num_pages = num_pages;
+  a->batch = batch;
+  a->total_tokens = batch;
+  a->max_q_len = 1;
+  a->max_seq_len = max_seq_len;
+  a->jmax = (int32_t)jmax_of(cfg, batch, max_seq_len);
+  a->ws_ml = (float2*)workspace;
+  a->ws_acc = (float*)((char*)workspace + ws_ml_bytes((int64_t)batch * cfg->num_q_heads, a->jmax));
+  return BI_OK;
+}
+
+int dispatch_partials(const bi_attn_cfg* cfg, const AttnParams& a, hipStream_t s) {
+  const bool bf = cfg->dtype == BI_BF16;
+  if (cfg->head_dim == 128) return bf ? launch_partials<__bf16, 128>(a, s) : launch_partials<float, 128>(a, s);
+  return bf ? launch_partials<__bf16, 64>(a, s) : launch_partials<float, 64>(a, s);
 }
 
 constexpr int kPrefillNBW = 2;
 
-template <typename E, int D>
+template <typename E, int D, int NW>
 int launch_prefill(const AttnParams& a, hipStream_t s) {
-  const int cols = kWaves * kPrefillNBW * 16;
+  const int cols = NW * kPrefillNBW * 16;
   const int tq = cols / a.group;
   const dim3 grid((unsigned)((a.max_q_len + tq - 1) / tq), (unsigned)a.hkv, (unsigned)a.batch);
-  hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW>), grid, dim3(kThreads), 0, s, a);
+  if (a.group >= 16) hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, false>), grid, dim3(64 * NW), 0, s, a);
+  else hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, true>), grid, dim3(64 * NW), 0, s, a);
   return launched();
 }
 
@@ -525,34 +661,34 @@ int bi_attn_decode(const bi_attn_cfg* cfg, const void* q, const void* k_cache, c
                    const int32_t* page_table, int32_t max_pages, int32_t num_pages,
                    const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float* out,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = check_cfg(cfg);
-  if (st != BI_OK) return st;
-  if (batch < 0 || max_seq_len < 0 || max_pages < 0 || num_pages < 0) return BI_EINVAL;
-  if (batch == 0) return BI_OK;
-  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out) return BI_EINVAL;
-  if (max_seq_len == 0 || max_pages == 0 || num_pages == 0) return BI_EINVAL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return BI_EINVAL;
-  const size_t need = ws_bytes(cfg, batch, batch, max_seq_len);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return BI_EWORKSPACE;
-  AttnParams a = base_params(cfg);
-  a.q = (const char*)q;
-  a.k_cache = (const char*)k_cache;
-  a.v_cache = (const char*)v_cache;
-  a.page_table = page_table;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  a.max_pages = max_pages;
-  a.num_pages = num_pages;
-  a.batch = batch;
-  a.total_tokens = batch;
-  a.max_q_len = 1;
-  a.max_seq_len = max_seq_len;
-  a.jmax = (int32_t)jmax_of(cfg, batch, max_seq_len);
-  a.ws_ml = (float2*)workspace;
-  a.ws_acc = (float*)((char*)workspace + ws_ml_bytes((int64_t)batch * cfg->num_q_heads, a.jmax));
-  const bool bf = cfg->dtype == BI_BF16;
-  if (cfg->head_dim == 128) return bf ? launch_decode<__bf16, 128>(a, stream) : launch_decode<float, 128>(a, stream);
-  return bf ? launch_decode<__bf16, 64>(a, stream) : launch_decode<float, 64>(a, stream);
+  AttnParams a;
+  const int st = decode_params(cfg, q, k_cache, v_cache, page_table, max_pages, num_pages, seq_lens,
+                               batch, max_seq_len, out, workspace, workspace_bytes, true, true, &a);
+  if (st != BI_OK) return st < 0 ? BI_OK : st;
+  if (dispatch_partials(cfg, a, stream) != BI_OK) return BI_EHIP;
+  return launch_combine(a, cfg->head_dim, stream);
+}
+
+int bi_attn_decode_partials(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* page_table, int32_t max_pages,
+                            int32_t num_pages, const int32_t* seq_lens, int32_t batch,
+                            int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  AttnParams a;
+  const int st = decode_params(cfg, q, k_cache, v_cache, page_table, max_pages, num_pages, seq_lens,
+                               batch, max_seq_len, nullptr, workspace, workspace_bytes, true, false, &a);
+  if (st != BI_OK) return st < 0 ? BI_OK : st;
+  return dispatch_partials(cfg, a, stream);
+}
+
+int bi_attn_decode_combine(const bi_attn_cfg* cfg, const int32_t* seq_lens, int32_t batch,
+                           int32_t max_seq_len, float* out, const void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  AttnParams a;
+  const int st = decode_params(cfg, nullptr, nullptr, nullptr, nullptr, 0, 0, seq_lens, batch,
+                               max_seq_len, out, workspace, workspace_bytes, false, true, &a);
+  if (st != BI_OK) return st < 0 ? BI_OK : st;
+  return launch_combine(a, cfg->head_dim, stream);
 }
 
 int bi_attn_prefill(const bi_attn_cfg* cfg, const void* q, const void* k_cache, const void* v_cache,
@@ -585,8 +721,8 @@ int bi_attn_prefill(const bi_attn_cfg* cfg, const void* q, const void* k_cache, 
   a.max_q_len = max_q_len;
   a.max_seq_len = max_seq_len;
   const bool bf = cfg->dtype == BI_BF16;
-  if (cfg->head_dim == 128) return bf ? launch_prefill<__bf16, 128>(a, stream) : launch_prefill<float, 128>(a, stream);
-  return bf ? launch_prefill<__bf16, 64>(a, stream) : launch_prefill<float, 64>(a, stream);
+  if (cfg->head_dim == 128) return bf ? launch_prefill<__bf16, 128, 8>(a, stream) : launch_prefill<float, 128, 4>(a, stream);
+  return bf ? launch_prefill<__bf16, 64, 8>(a, stream) : launch_prefill<float, 64, 4>(a, stream);
 }
 
 }  // extern "C"

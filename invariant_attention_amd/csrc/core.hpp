@@ -87,76 +87,88 @@ template <int D> struct Frag<__bf16, D> {
   static constexpr int NKS = D / 32;
   static constexpr int NM = D / 16;
   static constexpr int ROWB = D * 2;                 // bytes per K/V row
+  using KOp = u32x4;
+  using VRow = typename std::conditional<NM == 8, u32x4, u32x2>::type;  // dims [NM c, NM c + NM)
   struct Q { u32x4 v[NKS]; };
-  struct K { u32x4 v[2][NKS]; };
-  struct V { u32x4 v[NM]; };                         // A operand of PV per row block mb
-  // Raw V: for each of the lane's 8 keys, dims [NM c, NM c + NM).
-  using VRow = typename std::conditional<NM == 8, u32x4, u32x2>::type;
   struct VRaw { VRow v[8]; };
 
   __device__ static inline int vkey(int i, int g) { return (i < 4) ? (4 * g + i) : (16 + 4 * g + i - 4); }
-
+  // operand bytes of k-step st from a K (or q) row
+  __device__ static inline KOp k_op(const char* row, int st, int g) {
+    return *(const u32x4*)(row + (32 * st + 8 * g) * 2);
+  }
+  __device__ static inline KOp zero_k() { return u32x4{0, 0, 0, 0}; }
+  // raw V chunk of lane column c from a V row
+  __device__ static inline VRow v_row(const char* row, int c) { return *(const VRow*)(row + NM * c * 2); }
+  __device__ static inline VRow zero_v() { return VRow{}; }
   __device__ static inline void load_q(Q& q, const char* row, int g) {
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) q.v[s] = *(const u32x4*)(row + (32 * s + 8 * g) * 2);
+    for (int s = 0; s < NKS; ++s) q.v[s] = k_op(row, s, g);
   }
   __device__ static inline void zero_q(Q& q) {
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) q.v[s] = u32x4{0, 0, 0, 0};
+    for (int s = 0; s < NKS; ++s) q.v[s] = zero_k();
   }
-  // A-operand rows of key block kb: `row` points at the K row of key 16 kb + c.
-  __device__ static inline void load_k_block(K& k, int kb, const char* row, int g) {
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) k.v[kb][s] = *(const u32x4*)(row + (32 * s + 8 * g) * 2);
-  }
-  __device__ static inline void zero_k_block(K& k, int kb) {
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) k.v[kb][s] = u32x4{0, 0, 0, 0};
-  }
-  // `row` points at the V row of key vkey(i, g).
-  __device__ static inline void load_v_key(VRaw& r, int i, const char* row, int c) {
-    r.v[i] = *(const VRow*)(row + NM * c * 2);
-  }
-  __device__ static inline void zero_v_key(VRaw& r, int i) { r.v[i] = VRow{}; }
-  // Transpose raw V into the A operand of each row block: slot pair (2p, 2p+1) of block mb
-  // holds dim NM c + mb of keys vkey(2p), vkey(2p+1). Pure data movement.
-  __device__ static inline void pack_v(V& v, const VRaw& r) {
-#pragma unroll
-    for (int mb = 0; mb < NM; ++mb) {
-      const int w = mb >> 1;
-      unsigned out[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const unsigned a = r.v[2 * p][w], b = r.v[2 * p + 1][w];
-        out[p] = (mb & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      v.v[mb] = u32x4{out[0], out[1], out[2], out[3]};
-    }
-  }
-  __device__ static inline void qk(f32x4 s[2], const K& k, const Q& q) {
+  template <int NB, class KGet>
+  __device__ static inline void qk(f32x4 (&s)[NB][2], KGet& getK, const Q (&q)[NB]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < NKS; ++st) a = mma_bf16(k.v[kb][st], q.v[st], a);
-      s[kb] = a;
+      for (int b = 0; b < NB; ++b) s[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        const u32x4 kf = getK(kb, st);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) s[b][kb] = mma_bf16(kf, q[b].v[st], s[b][kb]);
+      }
     }
   }
   // acc += P V with P = P_hi + P_lo, both bf16 (round to nearest even), hi first.
-  __device__ static inline void pv(f32x4 acc[NM], const V& v, const float p[2][4]) {
-    unsigned hi[4], lo[4];
+  // getV(i, w2) returns dwords [2 w2, 2 w2 + 2) of the lane's raw V chunk for key slot i.
+  template <int NB, class VGet>
+  __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
+    u32x4 H[NB], L[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x0 = p[i >> 1][(2 * i) & 3], x1 = p[i >> 1][(2 * i + 1) & 3];
-      hi[i] = bf16_pack2(x0, x1);
-      lo[i] = bf16_pack2(x0 - bf16_lo_f(hi[i]), x1 - bf16_hi_f(hi[i]));
-    }
-    const u32x4 H = {hi[0], hi[1], hi[2], hi[3]}, L = {lo[0], lo[1], lo[2], lo[3]};
+    for (int b = 0; b < NB; ++b) {
+      unsigned hi[4], lo[4];
 #pragma unroll
-    for (int mb = 0; mb < NM; ++mb) {
-      acc[mb] = mma_bf16(v.v[mb], H, acc[mb]);
-      acc[mb] = mma_bf16(v.v[mb], L, acc[mb]);
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = p[b][i >> 1][(2 * i) & 3], x1 = p[b][i >> 1][(2 * i + 1) & 3];
+        hi[i] = bf16_pack2(x0, x1);
+        lo[i] = bf16_pack2(x0 - bf16_lo_f(hi[i]), x1 - bf16_hi_f(hi[i]));
+      }
+      H[b] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      L[b] = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
+#pragma unroll
+    for (int w2 = 0; w2 < NM / 4; ++w2) {
+      u32x2 d[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d[i] = getV(i, w2);
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) {
+        const int mb = 4 * w2 + m4;
+        const int h = m4 >> 1;           // dword within the pair
+        unsigned out[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const unsigned x = d[2 * q][h], y = d[2 * q + 1][h];
+          out[q] = (m4 & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+        }
+        const u32x4 vf = u32x4{out[0], out[1], out[2], out[3]};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          acc[b][mb] = mma_bf16(vf, H[b], acc[b][mb]);
+          acc[b][mb] = mma_bf16(vf, L[b], acc[b][mb]);
+        }
+      }
+    }
+  }
+  // dword pair w2 of a raw V chunk held in registers
+  __device__ static inline u32x2 v_pair(const VRow& r, int w2) { return u32x2{r[2 * w2], r[2 * w2 + 1]}; }
+  // dword pair w2 of the raw V chunk of lane column c in a V row
+  __device__ static inline u32x2 v_pair_at(const char* row, int c, int w2) {
+    return *(const u32x2*)(row + NM * c * 2 + 8 * w2);
   }
 };
 
@@ -166,13 +178,32 @@ template <int D> struct Frag<float, D> {
   static constexpr int NKS = D / 4;
   static constexpr int NM = D / 16;
   static constexpr int ROWB = D * 4;
+  using KOp = float;
+  struct VRow { float v[NM]; };
   struct Q { float v[NKS]; };
-  struct K { float v[2][NKS]; };
-  struct VRaw { float v[8][NM]; };   // key index kb*4 + r
-  struct V { float v[8][NM]; };
+  struct VRaw { VRow v[8]; };
 
   __device__ static inline int vkey(int i, int g) { return 16 * (i >> 2) + 4 * g + (i & 3); }
-
+  __device__ static inline KOp k_op(const char* row, int st, int g) {
+    return *(const float*)(row + (NKS * g + st) * 4);
+  }
+  __device__ static inline KOp zero_k() { return 0.f; }
+  __device__ static inline VRow v_row(const char* row, int c) {
+    VRow r;
+    const f32x4* p = (const f32x4*)(row + NM * c * 4);
+#pragma unroll
+    for (int s = 0; s < NM / 4; ++s) {
+      const f32x4 t = p[s];
+      r.v[4 * s] = t[0]; r.v[4 * s + 1] = t[1]; r.v[4 * s + 2] = t[2]; r.v[4 * s + 3] = t[3];
+    }
+    return r;
+  }
+  __device__ static inline VRow zero_v() {
+    VRow r;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) r.v[m] = 0.f;
+    return r;
+  }
   __device__ static inline void load_q(Q& q, const char* row, int g) {
     const f32x4* p = (const f32x4*)(row + (NKS * g) * 4);
 #pragma unroll
@@ -185,127 +216,160 @@ template <int D> struct Frag<float, D> {
 #pragma unroll
     for (int s = 0; s < NKS; ++s) q.v[s] = 0.f;
   }
-  __device__ static inline void load_k_block(K& k, int kb, const char* row, int g) {
-    const f32x4* p = (const f32x4*)(row + (NKS * g) * 4);
-#pragma unroll
-    for (int s = 0; s < NKS / 4; ++s) {
-      const f32x4 t = p[s];
-      k.v[kb][4 * s] = t[0]; k.v[kb][4 * s + 1] = t[1]; k.v[kb][4 * s + 2] = t[2]; k.v[kb][4 * s + 3] = t[3];
-    }
-  }
-  __device__ static inline void zero_k_block(K& k, int kb) {
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) k.v[kb][s] = 0.f;
-  }
-  __device__ static inline void load_v_key(VRaw& r, int i, const char* row, int c) {
-    const f32x4* p = (const f32x4*)(row + NM * c * 4);
-#pragma unroll
-    for (int s = 0; s < NM / 4; ++s) {
-      const f32x4 t = p[s];
-      r.v[i][4 * s] = t[0]; r.v[i][4 * s + 1] = t[1]; r.v[i][4 * s + 2] = t[2]; r.v[i][4 * s + 3] = t[3];
-    }
-  }
-  __device__ static inline void zero_v_key(VRaw& r, int i) {
-#pragma unroll
-    for (int m = 0; m < NM; ++m) r.v[i][m] = 0.f;
-  }
-  __device__ static inline void pack_v(V& v, const VRaw& r) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) v.v[i][m] = r.v[i][m];
-  }
-  __device__ static inline void qk(f32x4 s[2], const K& k, const Q& q) {
+  template <int NB, class KGet>
+  __device__ static inline void qk(f32x4 (&s)[NB][2], KGet& getK, const Q (&q)[NB]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < NKS; ++st) a = mma_f32(k.v[kb][st], q.v[st], a);
-      s[kb] = a;
+      for (int b = 0; b < NB; ++b) s[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        const float kf = getK(kb, st);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) s[b][kb] = mma_f32(kf, q[b].v[st], s[b][kb]);
+      }
     }
   }
-  __device__ static inline void pv(f32x4 acc[NM], const V& v, const float p[2][4]) {
+  // getV(i, 0) returns the lane's raw V chunk (NM floats) for key slot i.
+  template <int NB, class VGet>
+  __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const VRow row = getV(i, 0);
 #pragma unroll
-      for (int mb = 0; mb < NM; ++mb) acc[mb] = mma_f32(v.v[i][mb], p[i >> 2][i & 3], acc[mb]);
+      for (int mb = 0; mb < NM; ++mb)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][mb] = mma_f32(row.v[mb], p[b][i >> 2][i & 3], acc[b][mb]);
+    }
   }
+  __device__ static inline VRow v_pair(const VRow& r, int) { return r; }
+  __device__ static inline VRow v_pair_at(const char* row, int c, int) { return v_row(row, c); }
 };
 
 // ------------------------------------------------------------------------------------------
-// Softmax state of one query row (one lane group), in base-2 units: m is the running max of
-// q.k * c with c = scale * log2(e); p = 2^(q.k c - m); l = sum p; acc = sum p v.
+// Softmax state of one query row (one lane group), in base-2 units: p = 2^(q.k c - m) with
+// c = scale * log2(e); l = sum p; acc = sum p v. m is a reference maximum: it is set to the
+// sub-tile row max at the start of a split and raised only when a later row max exceeds it
+// by more than kLazy (so p <= 2^kLazy). The result is the same softmax; skipping most
+// rescales removes the acc *= alpha multiplies from most sub-tiles. The decision depends on
+// the row's own numbers only, so every route makes the same one.
+constexpr float kLazy = 8.0f;
+
 template <int D> struct RowState {
   static constexpr int NM = D / 16;
   float m, l;
   f32x4 acc[NM];
 };
 
-// One 32-key sub-tile of one column block.
-//   first:   this is the first sub-tile of the split (state is reset, not rescaled)
-//   mask:    some key of the sub-tile may lie after some row's position (wave-uniform)
-//   partial: some row of the block must keep its state unchanged (wave-uniform)
-//   key0:    absolute position of the sub-tile's first key; pos: this lane's row position
-//   active:  key0 <= pos for this lane's row (only read when `partial`)
-template <typename E, int D>
-__device__ __forceinline__ void subtile_step(RowState<D>& st, const typename Frag<E, D>::Q& q,
-                                             const typename Frag<E, D>::K& k,
-                                             const typename Frag<E, D>::V& v, float cscale,
-                                             int key0, int g, int pos, bool active, bool first,
-                                             bool mask, bool partial) {
+__device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballot_w64(v) != 0; }
+
+// One 32-key sub-tile of NB column blocks that share the K/V operands.
+//   getK(kb, s)   -> K operand of key block kb, k-step s
+//   getV(i, part) -> piece `part` of the lane's raw V chunk for key slot i
+//   pos[b]        -> this lane's row position in block b
+//   first: first sub-tile of the split (state reset, not rescaled)
+//   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
+//   SEL:   rows with pos < key0 keep their state (only when a block mixes such rows)
+template <typename E, int D, int NB, bool SEL, class KGet, class VGet>
+__device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Frag<E, D>::Q* q,
+                                             const int* pos, KGet&& getK, VGet&& getV,
+                                             float cscale, int key0, int g, bool first, bool mask) {
   using F = Frag<E, D>;
   constexpr int NM = D / 16;
-  f32x4 s[2];
-  F::qk(s, k, q);
-  float x[2][4];
+  typename F::Q qv[NB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int b = 0; b < NB; ++b) qv[b] = q[b];
+  f32x4 s[NB][2];
+  F::template qk<NB>(s, getK, qv);
+  float p[NB][2][4];
+  float mnew[NB], lnew[NB], alpha[NB];
+  bool need_any = false;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[kb][r] = s[kb][r];
-  if (mask) {
+  for (int b = 0; b < NB; ++b) {
+    float x[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        x[kb][r] = (key0 + 16 * kb + 4 * g + r <= pos) ? x[kb][r] : -__builtin_inff();
+      for (int r = 0; r < 4; ++r) x[kb][r] = s[b][kb][r];
+    if (mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[kb][r] = (key0 + 16 * kb + 4 * g + r <= pos[b]) ? x[kb][r] : -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    mx = xor_max(mx);
+    const float mt = mx * cscale;
+    bool need = false;
+    if (first) {
+      mnew[b] = mt;
+    } else {
+      need = mt > st[b].m + kLazy;
+      mnew[b] = need ? mt : st[b].m;
+    }
+    const float nm = -mnew[b];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[kb][r], cscale, nm));
+    float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
+               ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
+    rs = xor_sum(rs);
+    if (first) {
+      lnew[b] = rs;
+      alpha[b] = 0.f;
+    } else {
+      alpha[b] = need ? ex2(st[b].m - mnew[b]) : 1.0f;
+      lnew[b] = __builtin_fmaf(st[b].l, alpha[b], rs);
+    }
+    if (SEL && pos[b] < key0) need = false;
+    need_any = need_any || need;
   }
-  float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                   fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-  mx = xor_max(mx);
-  const float mnew = first ? mx * cscale : fmaxf(st.m, mx * cscale);
-  const float nm = -mnew;
-  float p[2][4];
+  if (SEL) {
+    f32x4 acc[NB][NM];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[kb][r] = ex2(__builtin_fmaf(x[kb][r], cscale, nm));
-  float rs = ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-  rs = xor_sum(rs);
-  f32x4 acc[NM];
-  float lnew;
-  if (first) {
-    lnew = rs;
+      for (int mb = 0; mb < NM; ++mb)
+        acc[b][mb] = first ? f32x4{0.f, 0.f, 0.f, 0.f} : st[b].acc[mb] * alpha[b];
+    F::template pv<NB>(acc, getV, p);
 #pragma unroll
-    for (int mb = 0; mb < NM; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else {
-    const float alpha = ex2(st.m - mnew);
-    lnew = __builtin_fmaf(st.l, alpha, rs);
+    for (int b = 0; b < NB; ++b) {
+      if (pos[b] >= key0) {
+        st[b].m = mnew[b];
+        st[b].l = lnew[b];
 #pragma unroll
-    for (int mb = 0; mb < NM; ++mb) acc[mb] = st.acc[mb] * alpha;
-  }
-  F::pv(acc, v, p);
-  if (partial) {
-    if (active) {
-      st.m = mnew;
-      st.l = lnew;
-#pragma unroll
-      for (int mb = 0; mb < NM; ++mb) st.acc[mb] = acc[mb];
+        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = acc[b][mb];
+      }
     }
   } else {
-    st.m = mnew;
-    st.l = lnew;
+    if (first) {
 #pragma unroll
-    for (int mb = 0; mb < NM; ++mb) st.acc[mb] = acc[mb];
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if (wave_any(need_any)) {
+      // alpha == 1 exactly for rows that kept their reference, so x * alpha == x
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
+    }
+    f32x4 accl[NB][NM];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int mb = 0; mb < NM; ++mb) accl[b][mb] = st[b].acc[mb];
+    F::template pv<NB>(accl, getV, p);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      st[b].m = mnew[b];
+      st[b].l = lnew[b];
+#pragma unroll
+      for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = accl[b][mb];
+    }
   }
 }
 
