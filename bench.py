@@ -41,6 +41,33 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("invariant_attention_amd/csrc/bi_attn.hip", "invariant_attention_amd/csrc/core.hpp",
+                  "include/bi_attn.h")
+
+
+def kernel_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summaries, if they were taken
+    on the kernel sources as they are now (else None)."""
+    import glob
+    import re
+    sha = kernel_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for m in re.finditer(r"<!-- traffic: (\{.*?\}) -->", open(path).read()):
+            rec = json.loads(m.group(1))
+            if rec.get("kernel_sha256") == sha and kernel in rec:
+                return rec[kernel]
+    return None
+
+
 def dev(x, dt):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dt)
 
@@ -170,7 +197,8 @@ def run_decode_bench(args, result):
     split_gbs = nb["split_kernel"] / (part * 1e-3) / 1e9
     result["roofline"] = {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1>",
                           "achieved": split_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": split_gbs / HBM_PEAK_GBS, "traffic": None,
+                          "frac": split_gbs / HBM_PEAK_GBS,
+                          "traffic": profiled_traffic("decode_split_kernel"),
                           "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": part}
     result["decode_breakdown_ms"] = {"page_update": pu, "partials": part, "combine": comb,
                                      "step_events": gpu_step, "step_wall": wall * 1e3}
@@ -269,7 +297,8 @@ def run_prefill_bench(args, result):
     }
     result["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel<bf16,128,2>",
                                   "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": tf / BF16_PEAK_TFLOPS, "traffic": None}
+                                  "frac": tf / BF16_PEAK_TFLOPS,
+                                  "traffic": profiled_traffic("prefill_kernel")}
     result["variant_slowdown"]["prefill"] = kern / kern_v - 1.0
     result["variant_slowdown"]["prefill_ms"] = {"invariant": kern, "split_by_batch": kern_v}
     return bt, ref
@@ -321,6 +350,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-samples", type=int, default=64)
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -336,6 +367,16 @@ def main():
               "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
               "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic (seeded N(0,1), bf16-rounded; no model weights)"}
+    if args.copy_calib_mb:
+        # a plain copy kernel of known size: reads and writes exactly n bytes each
+        n = args.copy_calib_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calib_bytes"] = n
+        del src, dst
     bt_dec, gpu_dec = run_decode_bench(args, result)
     log(f"decode: {result['value']:.0f} GB/s per step, split kernel "
         f"{result['roofline']['achieved']:.0f} GB/s")
