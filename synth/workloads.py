@@ -15,6 +15,8 @@ spare pages are filled with NaN so that any read of a slot that should not be re
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -211,10 +213,17 @@ def build_batch(shape: AttnShape, seqs: Sequence[SeqSpec], seed: int, *, page_se
     q = np.empty((T, Hq, D), np.float32)
     k_new = np.empty((T, Hkv, D), np.float32)
     v_new = np.empty((T, Hkv, D), np.float32)
+    # generate every prefix in parallel (numpy releases the GIL while filling arrays)
+    jobs = [(b, s, tensor) for b, s in enumerate(seqs) if fill_prefix and s.cached > 0
+            for tensor in ("k", "v")]
+    with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        prefix = dict(zip([(b, t) for b, _, t in jobs],
+                          ex.map(lambda j: token_values(seed, j[1].req, j[2], 0, j[1].cached, Hkv, D,
+                                                        shape.dtype), jobs)))
     for b, s in enumerate(seqs):
         if fill_prefix and s.cached > 0:
             for tensor, pool in (("k", k_pool), ("v", v_pool)):
-                vals = token_values(seed, s.req, tensor, 0, s.cached, Hkv, D, shape.dtype)
+                vals = prefix.pop((b, tensor))
                 npre = _pages_for(s.cached, P)
                 padded = np.full((npre * P, Hkv, D), np.nan, np.float32)
                 padded[: s.cached] = vals

@@ -1,0 +1,145 @@
+"""Mixed continuous-batching trace: every request's tokens bit-identical to running it alone.
+
+256 requests, 64 steps, at most 8192 tokens per step (decode tokens first, then FCFS prompt
+chunks), Hq 64, Hkv 4, D 128, page 16, split 256, pages freed and reused. Each step runs
+both ways the path allows — one prefill call with decode tokens as 1-token chunks, and one
+decode call plus one prefill call — and the two must agree bitwise. A subset of requests is
+then rerun alone at batch size 1 with the same chunk boundaries in a fresh pool, and a few
+of their tokens are checked against the fp64 oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_attention_amd as bi
+import oracle
+from synth import mixed_trace
+from synth.device import normal_tokens
+from synth.workloads import PageAllocator
+from gpu_harness import assert_bitwise, assert_parity, decode_workspace
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SEED = 2029
+HQ, HKV, D, P = 64, 4, 128, 16
+CFG = bi.AttnConfig(HQ, HKV, D, P, 256, bi.BI_BF16)
+NUM_PAGES = 48 * 1024
+
+
+def _entries(step, only=None):
+    ent = [(r, pos, 1, True) for r, pos in step.decode]
+    ent += [(r, start, n, False) for r, start, n in step.prefill]
+    if only is not None:
+        ent = [e for e in ent if e[0] == only]
+    return ent
+
+
+def _run_step(ent, alloc, kc, vc, mode):
+    """Page update + attention for one step; returns out [T][Hq][D] in entry order."""
+    dev = "cuda"
+    req = torch.tensor([r for r, s, n, _ in ent for _ in range(n)], device=dev)
+    pos = torch.tensor([p for r, s, n, _ in ent for p in range(s, s + n)], device=dev)
+    q = normal_tokens(SEED, req, "q", pos, HQ, D)
+    kn = normal_tokens(SEED, req, "k", pos, HKV, D)
+    vn = normal_tokens(SEED, req, "v", pos, HKV, D)
+    pages = [alloc.ensure(r, s + n, P) for r, s, n, _ in ent]
+    mp = max(len(p) for p in pages)
+    table = torch.full((len(ent), mp), -1, dtype=torch.int32)
+    for i, pg in enumerate(pages):
+        table[i, : len(pg)] = torch.tensor(pg, dtype=torch.int32)
+    table = table.to(dev)
+    sl = torch.tensor([s + n for r, s, n, _ in ent], dtype=torch.int32, device=dev)
+    qs = torch.tensor([0] + list(np.cumsum([n for _, _, n, _ in ent])), dtype=torch.int32, device=dev)
+    bi.bi_kv_page_update(CFG, kn, vn, qs, sl, table, kc, vc)
+    T = int(qs[-1])
+    mx = int(sl.max())
+    out = torch.full((T, HQ, D), float("nan"), device=dev)
+    if mode == "single":
+        bi.bi_attn_prefill(CFG, q, kc, vc, table, qs, sl, max(n for _, _, n, _ in ent), mx, out)
+        return out
+    dec = [i for i, e in enumerate(ent) if e[3]]
+    pre = [i for i, e in enumerate(ent) if not e[3]]
+    starts = qs.tolist()
+    if dec:
+        di = torch.tensor(dec, device=dev)
+        rows = torch.tensor([starts[i] for i in dec], device=dev)
+        od = torch.empty((len(dec), HQ, D), device=dev)
+        mxd = int(sl[di].max())
+        bi.bi_attn_decode(CFG, q[rows].contiguous(), kc, vc, table[di].contiguous(),
+                          sl[di].contiguous(), mxd, od, decode_workspace(CFG, len(dec), mxd))
+        out[rows] = od
+    if pre:
+        pi = torch.tensor(pre, device=dev)
+        rows = torch.cat([torch.arange(starts[i], starts[i + 1], device=dev) for i in pre])
+        qsp = torch.tensor([0] + list(np.cumsum([ent[i][2] for i in pre])), dtype=torch.int32, device=dev)
+        op = torch.empty((rows.numel(), HQ, D), device=dev)
+        bi.bi_attn_prefill(CFG, q[rows].contiguous(), kc, vc, table[pi].contiguous(), qsp,
+                           sl[pi].contiguous(), max(ent[i][2] for i in pre), int(sl[pi].max()), op)
+        out[rows] = op
+    return out
+
+
+def test_mixed_trace_requests_match_alone():
+    tr = mixed_trace(SEED)
+    kc = torch.full((NUM_PAGES, HKV, P, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    alloc = PageAllocator(NUM_PAGES, seed=SEED)
+    # requests to replay alone: early ones (prefill then decode), middle and late ones
+    seen = sorted({r for st in tr.steps for r, _, _, _ in _entries(st)})
+    subset = sorted(set(seen[:6] + seen[len(seen) // 2: len(seen) // 2 + 3] + seen[-3:]))
+    rec = {r: {} for r in subset}
+    total_tokens = 0
+    for si, st in enumerate(tr.steps):
+        ent = _entries(st)
+        a = _run_step(ent, alloc, kc, vc, "single")
+        b = _run_step(ent, alloc, kc, vc, "split")
+        assert_bitwise(a, b, f"step {si}: single prefill call vs decode + prefill calls")
+        off = 0
+        for r, s, n, _ in ent:
+            if r in rec:
+                rec[r][s] = a[off: off + n].clone()       # one chunk per step, keyed by start
+            off += n
+        total_tokens += sum(n for _, _, n, _ in ent)
+        for r in st.finished:
+            alloc.release(r)
+        if si % 8 == 0:
+            print(f"CASE trace step {si}: {len(ent)} sequences, {a.shape[0]} tokens", flush=True)
+    assert total_tokens > 64 * 8000
+    # the subset, each alone at batch size 1 in a fresh pool with different pages
+    for r in subset:
+        kc1 = torch.full((NUM_PAGES // 8, HKV, P, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vc1 = torch.full_like(kc1, float("nan"))
+        al1 = PageAllocator(NUM_PAGES // 8, seed=SEED + 1 + r)
+        for st in tr.steps:
+            ent = _entries(st, only=r)
+            if not ent:
+                continue
+            out = _run_step(ent, al1, kc1, vc1, "split")
+            s = ent[0][1]
+            assert_bitwise(out, rec[r][s], f"request {r} chunk at {s} alone vs batched")
+        print(f"CASE alone ok: request {r}, {sum(v.shape[0] for v in rec[r].values())} tokens",
+              flush=True)
+    # oracle parity on sampled tokens of two requests
+    for r in subset[:2]:
+        rows = {s + i: chunk[i] for s, chunk in rec[r].items() for i in range(chunk.shape[0])}
+        positions = sorted(rows)
+        sample = positions[:: max(1, len(positions) // 6)][:6]
+        L = sample[-1] + 1
+        req = torch.full((L,), r, device="cuda")
+        pos = torch.arange(L, device="cuda")
+        K = normal_tokens(SEED, req, "k", pos, HKV, D).float().cpu().numpy()
+        V = normal_tokens(SEED, req, "v", pos, HKV, D).float().cpu().numpy()
+        Q = normal_tokens(SEED, req, "q", pos, HQ, D).float().cpu().numpy()
+        npg = (L + P - 1) // P
+        pad = np.full((npg * P, HKV, D), np.nan, np.float32)
+        kp, vp = pad.copy(), pad.copy()
+        kp[:L], vp[:L] = K, V
+        kp = kp.reshape(npg, P, HKV, D).transpose(0, 2, 1, 3)
+        vp = vp.reshape(npg, P, HKV, D).transpose(0, 2, 1, 3)
+        table = np.arange(npg, dtype=np.int32)[None]
+        for p in sample:
+            ref = oracle.paged_attention(Q[p:p + 1], kp, vp, table, np.array([0, 1], np.int32),
+                                         np.array([p + 1], np.int32), HKV)
+            assert_parity(rows[p][None].cpu().numpy(), ref, f"request {r} position {p}")

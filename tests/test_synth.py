@@ -94,3 +94,27 @@ def test_page_allocator_reuses_freed_pages():
     al.release(0)
     c = al.ensure(2, 40, 16)
     assert set(c) <= set(a) | set(range(10)) and not set(c) & set(b)
+
+
+def test_device_generator_definition_and_moments():
+    """splitmix64 against its published definition in Python integers; N(0, 1) moments."""
+    from synth.device import normal_tokens, splitmix64
+
+    def ref(x):
+        m = (1 << 64) - 1
+        z = (x + 0x9E3779B97F4A7C15) & m
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+        return z ^ (z >> 31)
+
+    xs = [0, 1, 2, 12345, (1 << 63) - 1, 1 << 62, 0x0123456789ABCDEF]
+    got = splitmix64(torch.tensor([x - (1 << 64) if x >= 1 << 63 else x for x in xs], dtype=torch.int64))
+    assert [int(v) & ((1 << 64) - 1) for v in got] == [ref(x) for x in xs]
+    req = torch.arange(64).repeat_interleave(16)
+    pos = torch.arange(16).repeat(64)
+    z = normal_tokens(7, req, "k", pos, 4, 128, dtype=torch.float32)
+    assert abs(float(z.mean())) < 0.01 and abs(float(z.std()) - 1.0) < 0.01
+    # stateless: any subset of tokens regenerates the same values
+    z2 = normal_tokens(7, req[100:300], "k", pos[100:300], 4, 128, dtype=torch.float32)
+    assert torch.equal(z[100:300], z2)
+    assert not torch.equal(normal_tokens(7, req, "v", pos, 4, 128, dtype=torch.float32), z)
