@@ -349,6 +349,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="measure the prefill workload alone (no headline value)")
     ap.add_argument("--cpu-samples", type=int, default=64)
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -377,6 +379,12 @@ def main():
         torch.cuda.synchronize()
         result["copy_calib_bytes"] = n
         del src, dst
+    if args.prefill_only:
+        result["variant_slowdown"] = {}
+        run_prefill_bench(args, result)
+        log(f"prefill: {result['prefill']['kernel_tflops']:.1f} TFLOP/s (kernel)")
+        print(json.dumps(result), flush=True)
+        return
     bt_dec, gpu_dec = run_decode_bench(args, result)
     log(f"decode: {result['value']:.0f} GB/s per step, split kernel "
         f"{result['roofline']['achieved']:.0f} GB/s")

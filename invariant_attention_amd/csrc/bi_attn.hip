@@ -142,7 +142,10 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
         if (key0 + F::vkey(i, g) >= seq_len) buf.v[i] = F::zero_v();
     }
     auto getK = [&](int kb, int s2) { return buf.k[kb][s2]; };
-    auto getV = [&](int i, int part) { return F::v_pair(buf.v[i], part); };
+    auto getV = [&](int x) {
+      if constexpr (std::is_same<E, float>::value) return buf.v[x];
+      else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
+    };
     subtile_step<E, D, NB, false>(st, qf, posv, getK, getV, a.cscale, key0, g, t == 0,
                                   key0 + kSubTile - 1 > pos);
   };
@@ -231,26 +234,30 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
 // ascending order, folding each finished split into the row state. K/V sub-tiles are staged
 // in LDS and shared by all NW waves (the global loads of sub-tile u+1 are in flight while u
 // is computed); each wave holds NBW column blocks. The row accumulator A, touched only when
-// a split ends, lives in LDS next to the sequence's cached page ids.
+// a split ends, lives in LDS next to the sequence's cached page ids. For bf16 the PV operand
+// comes from the row-major V sub-tile through transposing LDS reads, which puts head dim
+// d = 16 mb + 4 g + r in accumulator (mb, r) of lane group g; for fp32 the layout is the
+// decode one, d = NM (4 g + r) + mb.
 template <int D, typename E> struct Lds {
   static constexpr int ROWB = D * (int)sizeof(E);
-  static constexpr int STRIDE = ROWB + 16;              // pad rows against bank conflicts
+  static constexpr int STRIDE = ROWB + 32;              // row pitch: conflict-free K and V reads
   static constexpr int TILE = kSubTile * STRIDE;        // one K or V sub-tile
 };
 constexpr int kPageCache = 2048;
 
-template <typename E, int D, int NBW, int NW, bool LANESEL>
+template <typename E, int D, int NBW, int NW, bool LANESEL, bool RING>
 __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
   using F = Frag<E, D>;
   using LD = Lds<D, E>;
+  constexpr bool BF = std::is_same<E, __bf16>::value;
   constexpr int NM = D / 16;
   constexpr int NT = 64 * NW;
   constexpr int COLS = NW * NBW * 16;
   constexpr int CHUNKS = LD::ROWB / 16;                  // 16-byte chunks per row
-  constexpr int TOTAL = 2 * kSubTile * CHUNKS;           // K and V chunks per sub-tile
-  constexpr int PER = (TOTAL + NT - 1) / NT;
+  constexpr int PAIRS = kSubTile * CHUNKS;               // (row, chunk) slots of a sub-tile
+  constexpr int PP = (PAIRS + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) char lds_kv[2][LD::TILE];
-  __shared__ f32x4 lds_A[NW][NBW][NM][64];               // [wave][block][float4 e][lane]
+  __shared__ f32x4 lds_A[NW][NBW][NM][64];               // [wave][block][row block][lane]
   __shared__ int lds_pages[kPageCache];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -303,62 +310,87 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
   }
 
   const int nsub = bad_seq ? 0 : (pos_max_wg + kSubTile) / kSubTile;
-  const int npg = min((nsub * kSubTile) / kPage, kPageCache);
-  for (int i = threadIdx.x; i < npg; i += NT) lds_pages[i] = page_of(a, b, i, seq_len);
+  // page ids of the logical pages the tile reads, in an LDS ring of kPageCache entries
+  // (logical page lp in slot lp % kPageCache), refilled half a ring ahead of use
+  const int npg_total = nsub * (kSubTile / kPage);
+  for (int i = threadIdx.x; i < min(npg_total, kPageCache); i += NT) lds_pages[i] = page_of(a, b, i, seq_len);
   __syncthreads();
 
-  u32x4 pre[PER];
-  auto stage_load = [&](int u) {
+  // staging: each thread owns the same (row, 16-byte chunk) slots of the K and V sub-tiles
+  const char* kbase = a.k_cache + kvh * head_stride;
+  const char* vbase = a.v_cache + kvh * head_stride;
+  // A ring of NPF register sets keeps NPF sub-tiles of loads in flight. The loop is unrolled
+  // by NPF so every set has a fixed name, and every stage issues exactly the same loads
+  // (absent rows and sub-tiles past the end read an in-bounds dummy row whose value is then
+  // replaced by zero), so the wait before each LDS store counts exactly the later loads.
+  constexpr int NPF = 4;
+  u32x4 preK[NPF][PP], preV[NPF][PP];
+  bool okK[NPF][PP], okV[NPF][PP];
+  const int last = max(nsub - 1, 0);
+  auto stage_load = [&](int u, u32x4 (&pk)[PP], u32x4 (&pv)[PP], bool (&ok_k)[PP], bool (&ok_v)[PP]) {
     const int key0 = u * kSubTile;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int idx = threadIdx.x + k * NT;
-      u32x4 val = {0, 0, 0, 0};
-      if (idx < TOTAL) {
-        const int which = idx / (kSubTile * CHUNKS);       // 0 = K, 1 = V
-        const int rem = idx - which * kSubTile * CHUNKS;
-        const int r = rem / CHUNKS, ch = rem - r * CHUNKS;
-        const int key = key0 + r;
-        const int lp = key / kPage;
-        const int page = lp < kPageCache ? lds_pages[lp] : page_of(a, b, lp, seq_len);
-        // V rows at or past seq_len and rows of absent pages stay zero, so no stale cache
-        // bytes reach an MFMA
-        if (page >= 0 && (which == 0 || key < seq_len)) {
-          const char* src = (which ? a.v_cache : a.k_cache) + (size_t)page * page_stride +
-                            kvh * head_stride + (key % kPage) * LD::ROWB + ch * 16;
-          val = *(const u32x4*)src;
-        }
-      }
-      pre[k] = val;
+    for (int k = 0; k < PP; ++k) {
+      const int pair = min(threadIdx.x + k * NT, PAIRS - 1);
+      const int r = pair / CHUNKS, ch = pair - r * CHUNKS;
+      const int key = key0 + r;
+      const int lp = key / kPage;
+      const int page = u <= last ? lds_pages[lp % kPageCache] : -1;
+      const bool kok = page >= 0, vok = kok && key < seq_len;
+      const size_t dummy = (size_t)(key % kPage) * LD::ROWB + ch * 16;   // inside page 0
+      const size_t off = (size_t)page * page_stride + dummy;
+      pk[k] = *(const u32x4*)(kbase + (kok ? off : dummy));
+      pv[k] = *(const u32x4*)(vbase + (vok ? off : dummy));
+      ok_k[k] = kok;
+      ok_v[k] = vok;
     }
   };
-  auto stage_store = [&]() {
+  // V rows at or past seq_len and rows of absent pages are stored as zero, so no stale cache
+  // bytes reach an MFMA (the select waits for the load only here, NPF sub-tiles later)
+  auto stage_store = [&](const u32x4 (&pk)[PP], const u32x4 (&pv)[PP], const bool (&ok_k)[PP],
+                         const bool (&ok_v)[PP]) {
+    const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int idx = threadIdx.x + k * NT;
-      if (idx < TOTAL) {
-        const int which = idx / (kSubTile * CHUNKS);
-        const int rem = idx - which * kSubTile * CHUNKS;
-        const int r = rem / CHUNKS, ch = rem - r * CHUNKS;
-        *(u32x4*)(&lds_kv[which][r * LD::STRIDE + ch * 16]) = pre[k];
+    for (int k = 0; k < PP; ++k) {
+      const int pair = threadIdx.x + k * NT;
+      if (pair < PAIRS) {
+        const int r = pair / CHUNKS, ch = pair - r * CHUNKS;
+        *(u32x4*)(&lds_kv[0][r * LD::STRIDE + ch * 16]) = ok_k[k] ? pk[k] : z;
+        *(u32x4*)(&lds_kv[1][r * LD::STRIDE + ch * 16]) = ok_v[k] ? pv[k] : z;
       }
     }
   };
 
-  if (nsub > 0) stage_load(0);
-  for (int u = 0; u < nsub; ++u) {
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) stage_load(i, preK[i], preV[i], okK[i], okV[i]);
+  for (int u0 = 0; u0 < nsub; u0 += NPF) {
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) {
+    const int u = u0 + i;
+    if (u >= nsub) break;
     const int key0 = u * kSubTile;
     const int j = key0 / S;
     const bool first = key0 == j * S;
     const bool last_of_split = key0 + kSubTile == (j + 1) * S || u + 1 == nsub;
-    stage_store();
+    // when the loads reach a new half of the page ring, fill the half after it; the slots
+    // it overwrites belong to pages no later load reads
+    const int lpn = (u + NPF) * (kSubTile / kPage);
+    if (RING && lpn % (kPageCache / 2) == 0 && lpn >= kPageCache / 2) {
+      const int base = lpn + kPageCache / 2;
+      for (int t = threadIdx.x; t < kPageCache / 2; t += NT)
+        if (base + t < npg_total) lds_pages[(base + t) % kPageCache] = page_of(a, b, base + t, seq_len);
+    }
+    stage_store(preK[i], preV[i], okK[i], okV[i]);
     __syncthreads();
-    if (u + 1 < nsub) stage_load(u + 1);
+    stage_load(u + NPF, preK[i], preV[i], okK[i], okV[i]);
     if (wave_max >= key0) {
       const char* kt = lds_kv[0];
       const char* vt = lds_kv[1];
       auto getK = [&](int kb, int s2) { return F::k_op(kt + (16 * kb + c) * LD::STRIDE, s2, g); };
-      auto getV = [&](int i, int part) { return F::v_pair_at(vt + F::vkey(i, g) * LD::STRIDE, c, part); };
+      auto getV = [&](int x) {
+        if constexpr (BF) return F::v_tr(vt, LD::STRIDE, x, c, g);
+        else return F::v_row(vt + F::vkey(x, g) * LD::STRIDE, c);
+      };
       if (key0 <= wave_min) {
         // every valid row of the wave reaches key0: all blocks advance together
         subtile_step<E, D, NBW, false>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
@@ -386,20 +418,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
           Mrow[cb] = M;
           Lrow[cb] = L;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+          for (int mb = 0; mb < NM; ++mb) {
+            f32x4& slot = lds_A[wave][cb][mb][lane];
+            f32x4 A = j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot;
 #pragma unroll
-            for (int m4 = 0; m4 < NM / 4; ++m4) {
-              f32x4& slot = lds_A[wave][cb][r * (NM / 4) + m4][lane];
-              f32x4 A = j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot;
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                A[e] = fold_elem(A[e], st[cb].acc[4 * m4 + e][r], fa, fb, j == 0);
-              slot = A;
-            }
+            for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb, j == 0);
+            slot = A;
+          }
         }
       }
     }
     __syncthreads();
+  }
   }
   // Epilogue: out = A / L for every valid row.
 #pragma unroll
@@ -407,18 +437,26 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
     const int col = (wave * NBW + cb) * 16 + c;
     const int tok = t0 + col / G;
     if (tok >= n_new) continue;
-    float* dst = a.out + ((size_t)(q0 + tok) * a.hq + kvh * G + col % G) * D + 4 * g * NM;
+    float* dst = a.out + ((size_t)(q0 + tok) * a.hq + kvh * G + col % G) * D;
     const bool ok = valid_c[cb];
+    f32x4 R[NM];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int mb = 0; mb < NM; ++mb) {
+      const f32x4 A = lds_A[wave][cb][mb][lane];
 #pragma unroll
-      for (int m4 = 0; m4 < NM / 4; ++m4) {
-        const f32x4 A = lds_A[wave][cb][r * (NM / 4) + m4][lane];
-        f32x4 v;
+      for (int e = 0; e < 4; ++e) R[mb][e] = ok ? A[e] / Lrow[cb] : __builtin_nanf("");
+    }
+    if constexpr (BF) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = ok ? A[e] / Lrow[cb] : __builtin_nanf("");
-        *(f32x4*)(dst + r * NM + 4 * m4) = v;
-      }
+      for (int mb = 0; mb < NM; ++mb) *(f32x4*)(dst + 16 * mb + 4 * g) = R[mb];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int m4 = 0; m4 < NM / 4; ++m4)
+          *(f32x4*)(dst + NM * (4 * g + r) + 4 * m4) =
+              f32x4{R[4 * m4][r], R[4 * m4 + 1][r], R[4 * m4 + 2][r], R[4 * m4 + 3][r]};
+    }
   }
 }
 
@@ -605,8 +643,15 @@ int launch_prefill(const AttnParams& a, hipStream_t s) {
   const int cols = NW * kPrefillNBW * 16;
   const int tq = cols / a.group;
   const dim3 grid((unsigned)((a.max_q_len + tq - 1) / tq), (unsigned)a.hkv, (unsigned)a.batch);
-  if (a.group >= 16) hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, false>), grid, dim3(64 * NW), 0, s, a);
-  else hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, true>), grid, dim3(64 * NW), 0, s, a);
+  // sequences longer than the LDS page-id ring need the kernel that refills it
+  const bool ring = (int64_t)a.max_seq_len + kSubTile > (int64_t)kPageCache * kPage;
+  if (a.group >= 16) {
+    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, false, true>), grid, dim3(64 * NW), 0, s, a);
+    else hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, false, false>), grid, dim3(64 * NW), 0, s, a);
+  } else {
+    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, true, true>), grid, dim3(64 * NW), 0, s, a);
+    else hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, true, false>), grid, dim3(64 * NW), 0, s, a);
+  }
   return launched();
 }
 

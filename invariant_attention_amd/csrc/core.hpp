@@ -53,23 +53,55 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 // exp2 on the transcendental unit (v_exp_f32): exp2(-inf) = +0, exp2(0) = 1.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Cross-lane exchanges for the row max and row sum, on the VALU (gfx950 lane swaps):
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second, v_permlane32_swap the upper half of the first with the lower half of the second.
+// Started from two copies of x, the pair (a, b) holds (x[l], x[l ^ 16]) resp. (x[l], x[l ^ 32])
+// ordered the same way in both partner lanes. Written as the instructions themselves (the
+// builtins' second result is not reliable in this compiler), with wait states around them.
+__device__ __forceinline__ void swap_rows16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
-// x + partner is commutative, so every lane of the group ends with the same bits.
+__device__ __forceinline__ void swap_halves32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// max of two finite-or-infinite floats (NaN never reaches these: masked scores are -inf).
+// Written as the instruction itself so the compiler does not canonicalise each input.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm volatile("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float xor_max(float v) {
+  float a = v, b = v;
+  swap_rows16(a, b);
+  v = vmax(a, b);
+  a = v;
+  b = v;
+  swap_halves32(a, b);
+  return vmax(a, b);
+}
+// Both partners add the same two values in the same order, so they get the same bits.
 __device__ __forceinline__ float xor_sum(float v) {
-  v = v + __shfl_xor(v, 16);
-  v = v + __shfl_xor(v, 32);
-  return v;
+  float a = v, b = v;
+  swap_rows16(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  swap_halves32(a, b);
+  return a + b;
 }
 
-// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; lo in bits 0..15.
 __device__ __forceinline__ unsigned bf16_pack2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (unsigned)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 __device__ __forceinline__ float bf16_lo_f(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi_f(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -124,7 +156,9 @@ template <int D> struct Frag<__bf16, D> {
     }
   }
   // acc += P V with P = P_hi + P_lo, both bf16 (round to nearest even), hi first.
-  // getV(i, w2) returns dwords [2 w2, 2 w2 + 2) of the lane's raw V chunk for key slot i.
+  // getV(mb) returns the A operand of row block mb: 8 bf16 of one head-dim row d for the key
+  // slots vkey(0..7, g). Which d a (row block, lane) holds is the caller's choice; each
+  // output element's dot product is the same whichever MFMA row computes it.
   template <int NB, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
     u32x4 H[NB], L[NB];
@@ -141,34 +175,43 @@ template <int D> struct Frag<__bf16, D> {
       L[b] = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
 #pragma unroll
-    for (int w2 = 0; w2 < NM / 4; ++w2) {
-      u32x2 d[8];
+    for (int mb = 0; mb < NM; ++mb) {
+      const u32x4 vf = getV(mb);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) d[i] = getV(i, w2);
-#pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) {
-        const int mb = 4 * w2 + m4;
-        const int h = m4 >> 1;           // dword within the pair
-        unsigned out[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const unsigned x = d[2 * q][h], y = d[2 * q + 1][h];
-          out[q] = (m4 & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        }
-        const u32x4 vf = u32x4{out[0], out[1], out[2], out[3]};
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          acc[b][mb] = mma_bf16(vf, H[b], acc[b][mb]);
-          acc[b][mb] = mma_bf16(vf, L[b], acc[b][mb]);
-        }
+      for (int b = 0; b < NB; ++b) {
+        acc[b][mb] = mma_bf16(vf, H[b], acc[b][mb]);
+        acc[b][mb] = mma_bf16(vf, L[b], acc[b][mb]);
       }
     }
   }
-  // dword pair w2 of a raw V chunk held in registers
-  __device__ static inline u32x2 v_pair(const VRow& r, int w2) { return u32x2{r[2 * w2], r[2 * w2 + 1]}; }
-  // dword pair w2 of the raw V chunk of lane column c in a V row
-  __device__ static inline u32x2 v_pair_at(const char* row, int c, int w2) {
-    return *(const u32x2*)(row + NM * c * 2 + 8 * w2);
+  // A operand of row block mb from raw V chunks in registers (row d = NM c + mb): slot pair
+  // (2p, 2p+1) takes dim mb of keys vkey(2p), vkey(2p+1). Pure data movement.
+  __device__ static inline u32x4 pack_v(const VRow (&r)[8], int mb) {
+    const int w = mb >> 1;
+    unsigned out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const unsigned a = r[2 * p][w], b = r[2 * p + 1][w];
+      out[p] = (mb & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    return u32x4{out[0], out[1], out[2], out[3]};
+  }
+  // A operand of row block mb straight from a row-major V sub-tile in LDS, for the head-dim
+  // mapping d = 16 mb + c, with two transposing reads (ds_read_b64_tr_b16). In each 16-lane
+  // group the read hands lane i element i % 4 of the 8-byte chunks named by lanes i / 4 + 4 k,
+  // k = 0..3; so when lane j names dims [16 mb + 4 (j % 4), +4) of key KEY(j / 4), lane c
+  // receives dim 16 mb + c of keys KEY(0..3). KEY(k) = 4 g + k gives slots 0..3 and
+  // 16 + 4 g + k slots 4..7, the keys the score layout left in this lane group.
+  __device__ static inline u32x4 v_tr(const char* vt, int stride, int mb, int c, int g) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int col = (16 * mb + 4 * (c & 3)) * 2;
+    const char* r0 = vt + (4 * g + (c >> 2)) * stride + col;
+    const char* r1 = r0 + 16 * stride;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)r0);
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)r1);
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
   }
 };
 
@@ -230,20 +273,18 @@ template <int D> struct Frag<float, D> {
       }
     }
   }
-  // getV(i, 0) returns the lane's raw V chunk (NM floats) for key slot i.
+  // getV(i) returns the lane's raw V chunk (NM floats, dims NM c .. NM c + NM) of key slot i.
   template <int NB, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const VRow row = getV(i, 0);
+      const VRow row = getV(i);
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b][mb] = mma_f32(row.v[mb], p[b][i >> 2][i & 3], acc[b][mb]);
     }
   }
-  __device__ static inline VRow v_pair(const VRow& r, int) { return r; }
-  __device__ static inline VRow v_pair_at(const char* row, int c, int) { return v_row(row, c); }
 };
 
 // ------------------------------------------------------------------------------------------
@@ -265,7 +306,7 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 
 // One 32-key sub-tile of NB column blocks that share the K/V operands.
 //   getK(kb, s)   -> K operand of key block kb, k-step s
-//   getV(i, part) -> piece `part` of the lane's raw V chunk for key slot i
+//   getV(x)       -> PV A operand (bf16: of row block x; fp32: raw V chunk of key slot x)
 //   pos[b]        -> this lane's row position in block b
 //   first: first sub-tile of the split (state reset, not rescaled)
 //   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
@@ -273,7 +314,8 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 template <typename E, int D, int NB, bool SEL, class KGet, class VGet>
 __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Frag<E, D>::Q* q,
                                              const int* pos, KGet&& getK, VGet&& getV,
-                                             float cscale, int key0, int g, bool first, bool mask) {
+                                             float cscale, int key0, int g, bool first,
+                                             bool mask) {
   using F = Frag<E, D>;
   constexpr int NM = D / 16;
   typename F::Q qv[NB];
@@ -298,8 +340,8 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
         for (int r = 0; r < 4; ++r)
           x[kb][r] = (key0 + 16 * kb + 4 * g + r <= pos[b]) ? x[kb][r] : -__builtin_inff();
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    float mx = vmax(vmax3(x[0][0], x[0][1], x[0][2]),
+                    vmax3(x[0][3], x[1][0], vmax3(x[1][1], x[1][2], x[1][3])));
     mx = xor_max(mx);
     const float mt = mx * cscale;
     bool need = false;
