@@ -55,6 +55,22 @@ __device__ __forceinline__ int page_of(const AttnParams& a, int b, int lp, int s
   return (p >= 0 && p < a.num_pages) ? p : -1;
 }
 
+// Rows read in place of a page that must not be dereferenced (table entry absent, outside the
+// pool, or past the sequence end). K rows are NaN, so a query row whose causal window needs the
+// page comes out NaN while masked keys ignore them; V rows are zero, so a zero probability
+// times V stays zero. Sized for the widest row (fp32, D 128). Loads are then unconditional.
+constexpr int kMaxRowBytes = 512;
+struct NanRows {
+  uint32_t w[kPage * kMaxRowBytes / 4];
+  constexpr NanRows() : w() {
+    for (int i = 0; i < kPage * kMaxRowBytes / 4; ++i) w[i] = 0x7fc07fc0u;   // bf16 and fp32 NaN
+  }
+};
+// (global, not constant, address space: a pointer that selects between them and a cache page
+// stays a global pointer, so its loads are global loads)
+__device__ __attribute__((aligned(256))) NanRows kNanRows;
+__device__ __attribute__((aligned(256))) uint32_t kZeroRows[kPage * kMaxRowBytes / 4];
+
 template <typename E, int D>
 __device__ __forceinline__ const char* kv_row(const char* cache, const AttnParams& a, int page,
                                               int kvh, int slot) {
@@ -72,7 +88,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   constexpr int NKS = F::NKS;
   constexpr int NM = D / 16;
   constexpr int ROWB = F::ROWB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
   const int c = lane & 15, g = lane >> 4;
   const int b = blockIdx.z, kvh = blockIdx.y;
   const int j = blockIdx.x * kWaves + wave;
@@ -89,9 +106,12 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   const char* kbase = a.k_cache + kvh * head_stride;
   const char* vbase = a.v_cache + kvh * head_stride;
 
-  // physical pages of the split, one logical page per lane, 64 at a time
+  // Every load below is unconditional: absent pages read kNanRows / kZeroRows and heads past
+  // the group read zero q, so no branch separates a buffer's loads from their use, and the
+  // loads of the next sub-tile stay in flight while the current one is computed.
+  const char* nan_rows = (const char*)&kNanRows;
+  const char* zero_rows = (const char*)kZeroRows;
   const int lp0 = k_begin / kPage;
-  int pg = page_of(a, b, lp0 + lane, seq_len);
 
   typename F::Q qf[NB];
   RowState<D> st[NB];
@@ -100,38 +120,14 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   for (int cb = 0; cb < NB; ++cb) {
     posv[cb] = pos;
     const int hl = cb * 16 + c;   // head within the group
-    if (hl < a.group) {
-      const char* row = a.q + ((size_t)b * a.hq + kvh * a.group + hl) * (size_t)ROWB;
-      F::load_q(qf[cb], row, g);
-    } else {
-      F::zero_q(qf[cb]);
-    }
+    const char* row = hl < a.group ? a.q + ((size_t)b * a.hq + kvh * a.group + hl) * (size_t)ROWB
+                                   : zero_rows;
+    F::load_q(qf[cb], row, g);
   }
 
   struct Buf {
     KOp k[2][NKS];
     VRow v[8];
-  };
-  auto fetch = [&](Buf& buf, int t) {
-    if (t > 0 && (t & 31) == 0) pg = page_of(a, b, lp0 + 2 * t + lane, seq_len);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int page = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
-      if (page >= 0) {
-        const char* kp = kbase + (size_t)page * page_stride;
-        const char* vp = vbase + (size_t)page * page_stride;
-#pragma unroll
-        for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
-#pragma unroll
-        for (int i = 4 * kb; i < 4 * kb + 4; ++i)
-          buf.v[i] = F::v_row(vp + (F::vkey(i, g) - 16 * kb) * ROWB, c);
-      } else {
-#pragma unroll
-        for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::zero_k();
-#pragma unroll
-        for (int i = 4 * kb; i < 4 * kb + 4; ++i) buf.v[i] = F::zero_v();
-      }
-    }
   };
   auto compute = [&](Buf& buf, int t) {
     const int key0 = k_begin + kSubTile * t;
@@ -150,14 +146,34 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
                                   key0 + kSubTile - 1 > pos);
   };
 
-  Buf b0, b1;
-  fetch(b0, 0);
-  for (int t = 0; t < nsub; t += 2) {
-    if (t + 1 < nsub) fetch(b1, t + 1);
-    compute(b0, t);
-    if (t + 1 >= nsub) break;
-    if (t + 2 < nsub) fetch(b0, t + 2);
-    compute(b1, t + 1);
+  // Windows of 32 sub-tiles: the window's 64 physical page ids, one per lane.
+  for (int w0 = 0; w0 < nsub; w0 += 32) {
+    const int nw = min(32, nsub - w0);
+    const int pg = page_of(a, b, lp0 + 2 * w0 + lane, seq_len);
+    // sub-tile t of the window; t >= nw (the loads issued past the end) reads the stand-ins
+    auto fetch = [&](Buf& buf, int t) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int pl = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
+        const int page = t < nw ? pl : -1;
+        const char* kp = page >= 0 ? kbase + (size_t)page * page_stride : nan_rows;
+        const char* vp = page >= 0 ? vbase + (size_t)page * page_stride : zero_rows;
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
+#pragma unroll
+        for (int i = 4 * kb; i < 4 * kb + 4; ++i)
+          buf.v[i] = F::v_row(vp + (F::vkey(i, g) - 16 * kb) * ROWB, c);
+      }
+    };
+    Buf b0, b1;
+    fetch(b0, 0);
+    for (int t = 0; t < nw; t += 2) {
+      fetch(b1, t + 1);
+      compute(b0, w0 + t);
+      if (t + 1 >= nw) break;
+      fetch(b0, t + 2);
+      compute(b1, w0 + t + 1);
+    }
   }
 
   // Partial of split j for every real head of the block.
@@ -320,14 +336,16 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
   const char* kbase = a.k_cache + kvh * head_stride;
   const char* vbase = a.v_cache + kvh * head_stride;
   // A ring of NPF register sets keeps NPF sub-tiles of loads in flight. The loop is unrolled
-  // by NPF so every set has a fixed name, and every stage issues exactly the same loads
-  // (absent rows and sub-tiles past the end read an in-bounds dummy row whose value is then
-  // replaced by zero), so the wait before each LDS store counts exactly the later loads.
+  // by NPF so every set has a fixed name, and every stage issues exactly the same loads, so
+  // the wait before each LDS store counts exactly the later loads. Absent pages and sub-tiles
+  // past the end read kNanRows (K) and kZeroRows (V), and so do V rows at or past seq_len:
+  // no stale cache bytes reach an MFMA, and a row that needs an absent page comes out NaN.
   constexpr int NPF = 4;
   u32x4 preK[NPF][PP], preV[NPF][PP];
-  bool okK[NPF][PP], okV[NPF][PP];
   const int last = max(nsub - 1, 0);
-  auto stage_load = [&](int u, u32x4 (&pk)[PP], u32x4 (&pv)[PP], bool (&ok_k)[PP], bool (&ok_v)[PP]) {
+  const char* nan_rows = (const char*)&kNanRows;
+  const char* zero_rows = (const char*)kZeroRows;
+  auto stage_load = [&](int u, u32x4 (&pk)[PP], u32x4 (&pv)[PP]) {
     const int key0 = u * kSubTile;
 #pragma unroll
     for (int k = 0; k < PP; ++k) {
@@ -336,33 +354,26 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
       const int key = key0 + r;
       const int lp = key / kPage;
       const int page = u <= last ? lds_pages[lp % kPageCache] : -1;
-      const bool kok = page >= 0, vok = kok && key < seq_len;
-      const size_t dummy = (size_t)(key % kPage) * LD::ROWB + ch * 16;   // inside page 0
-      const size_t off = (size_t)page * page_stride + dummy;
-      pk[k] = *(const u32x4*)(kbase + (kok ? off : dummy));
-      pv[k] = *(const u32x4*)(vbase + (vok ? off : dummy));
-      ok_k[k] = kok;
-      ok_v[k] = vok;
+      const size_t in_page = (size_t)(key % kPage) * LD::ROWB + ch * 16;
+      const size_t off = (size_t)page * page_stride + in_page;
+      pk[k] = *(const u32x4*)(page >= 0 ? kbase + off : nan_rows + in_page);
+      pv[k] = *(const u32x4*)(page >= 0 && key < seq_len ? vbase + off : zero_rows + in_page);
     }
   };
-  // V rows at or past seq_len and rows of absent pages are stored as zero, so no stale cache
-  // bytes reach an MFMA (the select waits for the load only here, NPF sub-tiles later)
-  auto stage_store = [&](const u32x4 (&pk)[PP], const u32x4 (&pv)[PP], const bool (&ok_k)[PP],
-                         const bool (&ok_v)[PP]) {
-    const u32x4 z = {0, 0, 0, 0};
+  auto stage_store = [&](const u32x4 (&pk)[PP], const u32x4 (&pv)[PP]) {
 #pragma unroll
     for (int k = 0; k < PP; ++k) {
       const int pair = threadIdx.x + k * NT;
       if (pair < PAIRS) {
         const int r = pair / CHUNKS, ch = pair - r * CHUNKS;
-        *(u32x4*)(&lds_kv[0][r * LD::STRIDE + ch * 16]) = ok_k[k] ? pk[k] : z;
-        *(u32x4*)(&lds_kv[1][r * LD::STRIDE + ch * 16]) = ok_v[k] ? pv[k] : z;
+        *(u32x4*)(&lds_kv[0][r * LD::STRIDE + ch * 16]) = pk[k];
+        *(u32x4*)(&lds_kv[1][r * LD::STRIDE + ch * 16]) = pv[k];
       }
     }
   };
 
 #pragma unroll
-  for (int i = 0; i < NPF; ++i) stage_load(i, preK[i], preV[i], okK[i], okV[i]);
+  for (int i = 0; i < NPF; ++i) stage_load(i, preK[i], preV[i]);
   for (int u0 = 0; u0 < nsub; u0 += NPF) {
 #pragma unroll
   for (int i = 0; i < NPF; ++i) {
@@ -380,9 +391,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
       for (int t = threadIdx.x; t < kPageCache / 2; t += NT)
         if (base + t < npg_total) lds_pages[(base + t) % kPageCache] = page_of(a, b, base + t, seq_len);
     }
-    stage_store(preK[i], preV[i], okK[i], okV[i]);
+    stage_store(preK[i], preV[i]);
     __syncthreads();
-    stage_load(u + NPF, preK[i], preV[i], okK[i], okV[i]);
+    stage_load(u + NPF, preK[i], preV[i]);
     if (wave_max >= key0) {
       const char* kt = lds_kv[0];
       const char* vt = lds_kv[1];

@@ -59,24 +59,20 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // Started from two copies of x, the pair (a, b) holds (x[l], x[l ^ 16]) resp. (x[l], x[l ^ 32])
 // ordered the same way in both partner lanes. Written as the instructions themselves (the
 // builtins' second result is not reliable in this compiler), with wait states around them.
+// Their inputs are always VALU results, never MFMA results: the compiler inserts no MFMA
+// wait states in front of an asm block.
 __device__ __forceinline__ void swap_rows16(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
 __device__ __forceinline__ void swap_halves32(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
-// max of two finite-or-infinite floats (NaN never reaches these: masked scores are -inf).
-// Written as the instruction itself so the compiler does not canonicalise each input.
-__device__ __forceinline__ float vmax(float a, float b) {
-  float r;
-  asm volatile("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// IEEE 754-2019 maximum (a NaN input gives NaN; -0 < +0): gfx950's v_maximum3_f32, which needs
+// no canonicalising of its inputs. Kept as compiler-visible operations (not inline asm) because
+// their inputs are MFMA results, and only the compiler inserts the wait states an MFMA result
+// needs before a VALU instruction may read it.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 __device__ __forceinline__ float xor_max(float v) {
   float a = v, b = v;
   swap_rows16(a, b);

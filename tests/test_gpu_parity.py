@@ -119,3 +119,38 @@ def test_long_decode_sampled_rows():
     ref = oracle_rows(bt, rows)
     got = np.stack([out[t, h] for t, h in rows])
     assert_parity(got, ref, "long decode rows")
+
+
+@pytest.mark.parametrize("bad", ["negative", "past_pool"])
+def test_bad_page_entry_gives_nan_rows_only_where_needed(bad):
+    """A table entry outside [0, num_pages) is never dereferenced: query rows whose causal
+    window reaches that page come out NaN, every other row is bit-identical to a clean run."""
+    shape = AttnShape(16, 2, 128, page_size=16, split_size=64, dtype="bf16")
+    cfg = cfg_for(shape)
+    # sequence 1: 100 cached + 60 new tokens (positions 100..159); page 8 holds keys 128..143
+    seqs = [SeqSpec(0, 70, 5), SeqSpec(1, 100, 60), SeqSpec(2, 300, 9)]
+    bt = build_batch(shape, seqs, seed=31, page_seed=32, extra_pages=4)
+    clean = run_prefill(cfg, to_device(bt, cfg))
+    d = to_device(bt, cfg)
+    n_pages = d.k_cache.shape[0]
+    d.page_table[1, 8] = -7 if bad == "negative" else n_pages + 3
+    _print_case("bad page prefill", bad)
+    got = run_prefill(cfg, d)
+    r0, r1 = bt.token_rows(1)
+    pos = np.arange(100, 160)
+    need = pos >= 128
+    g = got[r0:r1].cpu()
+    assert torch.isnan(g[torch.from_numpy(need)]).all(), "rows needing the bad page must be NaN"
+    ok_rows = torch.cat([got[:r0], got[r0:r1][torch.from_numpy(~need).cuda()], got[r1:]])
+    ok_ref = torch.cat([clean[:r0], clean[r0:r1][torch.from_numpy(~need).cuda()], clean[r1:]])
+    assert_bitwise(ok_rows, ok_ref, f"rows not reaching the bad page ({bad})")
+    # decode: the last token of each sequence; only sequence 1 reaches page 8
+    dseqs = [SeqSpec(0, 74, 1), SeqSpec(1, 159, 1), SeqSpec(2, 308, 1)]
+    bd = build_batch(shape, dseqs, seed=33, page_seed=34, extra_pages=4)
+    clean_d = run_decode(cfg, to_device(bd, cfg))
+    dd = to_device(bd, cfg)
+    dd.page_table[1, 8] = -7 if bad == "negative" else dd.k_cache.shape[0] + 3
+    _print_case("bad page decode", bad)
+    got_d = run_decode(cfg, dd)
+    assert torch.isnan(got_d[1]).all()
+    assert_bitwise(got_d[[0, 2]], clean_d[[0, 2]], f"decode rows of other sequences ({bad})")
