@@ -12,6 +12,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/bi_attn.h"
 #include "core.hpp"
 
@@ -78,8 +80,26 @@ __device__ __forceinline__ const char* kv_row(const char* cache, const AttnParam
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode: one wave per split. Operands stream from HBM straight into MFMA registers, two
-// sub-tiles in flight: the loads of sub-tile t+1 are issued before sub-tile t is computed.
+// Decode. The work items of a KV head are the splits (b, j) of every sequence, in ascending b
+// and then j. The grid holds as many waves as the device keeps resident; wave w of a head takes
+// the k = ceil(items / waves) consecutive items from w k, so every launched wave has work (no
+// workgroup exits at once) and all of them finish after about k items. Per item, operands
+// stream from HBM straight into MFMA registers with two sub-tiles in flight: the loads of
+// sub-tile t+1 are issued before sub-tile t is computed.
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
 template <typename E, int D, int NB>
 __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void decode_split_kernel(AttnParams a) {
   using F = Frag<E, D>;
@@ -89,109 +109,157 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   constexpr int NM = D / 16;
   constexpr int ROWB = F::ROWB;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
   const int c = lane & 15, g = lane >> 4;
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int j = blockIdx.x * kWaves + wave;
-  const int seq_len = a.seq_lens[b];
-  if (seq_len <= 0 || seq_len > a.max_seq_len) return;   // combine writes NaN for the row
-  const int pos = seq_len - 1;
-  const int S = split_len(a, seq_len);
-  const int k_begin = j * S;
-  if (k_begin > pos || j >= a.jmax) return;
-  const int k_end = min(k_begin + S, pos + 1);
-  const int nsub = (k_end - k_begin + kSubTile - 1) / kSubTile;
+  const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
+  const int W = (int)(gridDim.x * kWaves) / a.hkv;             // waves per KV head
+  if (gw >= W * a.hkv) return;
+  const int kvh = gw % a.hkv, w = gw / a.hkv;
+
+  // Sequences are read 64 at a time, one per lane: length and split count (0 when the length
+  // is out of range; the combine writes NaN for such a row).
+  auto chunk_len = [&](int cb) {
+    const int bb = cb + lane;
+    return bb < a.batch ? a.seq_lens[bb] : 0;
+  };
+  auto splits_of = [&](int len) {
+    return (len > 0 && len <= a.max_seq_len) ? (len - 1) / split_len(a, len) + 1 : 0;
+  };
+  int total = 0;
+  for (int cb = 0; cb < a.batch; cb += 64) total += wave_sum_i(splits_of(chunk_len(cb)));
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int k = (total + W - 1) / W;
+  const int i0 = w * k;
+  if (i0 >= total) return;
+  const int n_items = min(k, total - i0);
+  // item i0: sequence b, split j
+  int cb = 0, before = 0, len_v = 0, nj_v = 0, b = 0, j = 0;
+  for (;;) {
+    len_v = chunk_len(cb);
+    nj_v = splits_of(len_v);
+    const int incl = wave_incl_scan(nj_v, lane);
+    const int tot = __builtin_amdgcn_readlane(incl, 63);
+    if (before + tot > i0) {
+      const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before + incl <= i0));
+      b = cb + nb;
+      j = i0 - before - (nb > 0 ? __builtin_amdgcn_readlane(incl, nb - 1) : 0);
+      break;
+    }
+    before += tot;
+    cb += 64;
+  }
+
   const size_t head_stride = (size_t)kPage * ROWB;
   const size_t page_stride = (size_t)a.hkv * head_stride;
   const char* kbase = a.k_cache + kvh * head_stride;
   const char* vbase = a.v_cache + kvh * head_stride;
-
   // Every load below is unconditional: absent pages read kNanRows / kZeroRows and heads past
   // the group read zero q, so no branch separates a buffer's loads from their use, and the
   // loads of the next sub-tile stay in flight while the current one is computed.
   const char* nan_rows = (const char*)&kNanRows;
   const char* zero_rows = (const char*)kZeroRows;
-  const int lp0 = k_begin / kPage;
-
-  typename F::Q qf[NB];
-  RowState<D> st[NB];
-  int posv[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    posv[cb] = pos;
-    const int hl = cb * 16 + c;   // head within the group
-    const char* row = hl < a.group ? a.q + ((size_t)b * a.hq + kvh * a.group + hl) * (size_t)ROWB
-                                   : zero_rows;
-    F::load_q(qf[cb], row, g);
-  }
-
   struct Buf {
     KOp k[2][NKS];
     VRow v[8];
   };
-  auto compute = [&](Buf& buf, int t) {
-    const int key0 = k_begin + kSubTile * t;
-    if (key0 + kSubTile > seq_len) {
-      // stale slots past the sequence end: V rows become zero, scores are masked below
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (key0 + F::vkey(i, g) >= seq_len) buf.v[i] = F::zero_v();
-    }
-    auto getK = [&](int kb, int s2) { return buf.k[kb][s2]; };
-    auto getV = [&](int x) {
-      if constexpr (std::is_same<E, float>::value) return buf.v[x];
-      else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
-    };
-    subtile_step<E, D, NB, false>(st, qf, posv, getK, getV, a.cscale, key0, g, t == 0,
-                                  key0 + kSubTile - 1 > pos);
-  };
 
-  // Windows of 32 sub-tiles: the window's 64 physical page ids, one per lane.
-  for (int w0 = 0; w0 < nsub; w0 += 32) {
-    const int nw = min(32, nsub - w0);
-    const int pg = page_of(a, b, lp0 + 2 * w0 + lane, seq_len);
-    // sub-tile t of the window; t >= nw (the loads issued past the end) reads the stand-ins
-    auto fetch = [&](Buf& buf, int t) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int pl = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
-        const int page = t < nw ? pl : -1;
-        const char* kp = page >= 0 ? kbase + (size_t)page * page_stride : nan_rows;
-        const char* vp = page >= 0 ? vbase + (size_t)page * page_stride : zero_rows;
-#pragma unroll
-        for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
-#pragma unroll
-        for (int i = 4 * kb; i < 4 * kb + 4; ++i)
-          buf.v[i] = F::v_row(vp + (F::vkey(i, g) - 16 * kb) * ROWB, c);
-      }
-    };
-    Buf b0, b1;
-    fetch(b0, 0);
-    for (int t = 0; t < nw; t += 2) {
-      fetch(b1, t + 1);
-      compute(b0, w0 + t);
-      if (t + 1 >= nw) break;
-      fetch(b0, t + 2);
-      compute(b1, w0 + t + 1);
-    }
-  }
+  for (int it = 0; it < n_items; ++it) {
+    const int seq_len = __builtin_amdgcn_readlane(len_v, b - cb);
+    const int pos = seq_len - 1;
+    const int S = split_len(a, seq_len);
+    const int k_begin = j * S;
+    const int k_end = min(k_begin + S, seq_len);
+    const int nsub = (k_end - k_begin + kSubTile - 1) / kSubTile;
+    const int lp0 = k_begin / kPage;
 
-  // Partial of split j for every real head of the block.
+    typename F::Q qf[NB];
+    RowState<D> st[NB];
+    int posv[NB];
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const int hl = cb * 16 + c;
-    if (hl >= a.group) continue;
-    const size_t row = (size_t)b * a.hq + kvh * a.group + hl;
-    const size_t pidx = row * a.jmax + j;
-    float* dst = a.ws_acc + pidx * D + 4 * g * NM;
+    for (int cq = 0; cq < NB; ++cq) {
+      posv[cq] = pos;
+      const int hl = cq * 16 + c;   // head within the group
+      const char* row = hl < a.group ? a.q + ((size_t)b * a.hq + kvh * a.group + hl) * (size_t)ROWB
+                                     : zero_rows;
+      F::load_q(qf[cq], row, g);
+    }
+
+    auto compute = [&](Buf& buf, int t) {
+      const int key0 = k_begin + kSubTile * t;
+      if (key0 + kSubTile > seq_len) {
+        // stale slots past the sequence end: V rows become zero, scores are masked below
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int mb = 0; mb < NM; mb += 4) {
-        f32x4 v = {st[cb].acc[mb][r], st[cb].acc[mb + 1][r], st[cb].acc[mb + 2][r], st[cb].acc[mb + 3][r]};
-        *(f32x4*)(dst + r * NM + mb) = v;
+        for (int i = 0; i < 8; ++i)
+          if (key0 + F::vkey(i, g) >= seq_len) buf.v[i] = F::zero_v();
       }
-    if (g == 0) a.ws_ml[pidx] = make_float2(st[cb].m, st[cb].l);
+      auto getK = [&](int kb, int s2) { return buf.k[kb][s2]; };
+      auto getV = [&](int x) {
+        if constexpr (std::is_same<E, float>::value) return buf.v[x];
+        else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
+      };
+      subtile_step<E, D, NB, false>(st, qf, posv, getK, getV, a.cscale, key0, g, t == 0,
+                                    key0 + kSubTile - 1 > pos);
+    };
+
+    // Windows of 32 sub-tiles: the window's 64 physical page ids, one per lane.
+    for (int w0 = 0; w0 < nsub; w0 += 32) {
+      const int nw = min(32, nsub - w0);
+      const int pg = page_of(a, b, lp0 + 2 * w0 + lane, seq_len);
+      // sub-tile t of the window; t >= nw (the loads issued past the end) reads the stand-ins
+      auto fetch = [&](Buf& buf, int t) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int pl = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
+          const int page = t < nw ? pl : -1;
+          const char* kp = page >= 0 ? kbase + (size_t)page * page_stride : nan_rows;
+          const char* vp = page >= 0 ? vbase + (size_t)page * page_stride : zero_rows;
+#pragma unroll
+          for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
+#pragma unroll
+          for (int i = 4 * kb; i < 4 * kb + 4; ++i)
+            buf.v[i] = F::v_row(vp + (F::vkey(i, g) - 16 * kb) * ROWB, c);
+        }
+      };
+      Buf b0, b1;
+      fetch(b0, 0);
+      for (int t = 0; t < nw; t += 2) {
+        fetch(b1, t + 1);
+        compute(b0, w0 + t);
+        if (t + 1 >= nw) break;
+        fetch(b0, t + 2);
+        compute(b1, w0 + t + 1);
+      }
+    }
+
+    // Partial of split j for every real head of the block.
+#pragma unroll
+    for (int cq = 0; cq < NB; ++cq) {
+      const int hl = cq * 16 + c;
+      if (hl >= a.group) continue;
+      const size_t row = (size_t)b * a.hq + kvh * a.group + hl;
+      const size_t pidx = row * a.jmax + j;
+      float* dst = a.ws_acc + pidx * D + 4 * g * NM;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int mb = 0; mb < NM; mb += 4) {
+          f32x4 v = {st[cq].acc[mb][r], st[cq].acc[mb + 1][r], st[cq].acc[mb + 2][r], st[cq].acc[mb + 3][r]};
+          *(f32x4*)(dst + r * NM + mb) = v;
+        }
+      if (g == 0) a.ws_ml[pidx] = make_float2(st[cq].m, st[cq].l);
+    }
+
+    // next item: the next split of this sequence, else split 0 of the next sequence with splits
+    if (++j >= __builtin_amdgcn_readlane(nj_v, b - cb)) {
+      j = 0;
+      do {
+        ++b;
+        if (b - cb >= 64) {
+          cb += 64;
+          len_v = chunk_len(cb);
+          nj_v = splits_of(len_v);
+        }
+      } while (b < a.batch && __builtin_amdgcn_readlane(nj_v, b - cb) == 0);
+    }
   }
 }
 
@@ -588,13 +656,33 @@ AttnParams base_params(const bi_attn_cfg* c) {
 
 int launched() { return hipGetLastError() == hipSuccess ? BI_OK : BI_EHIP; }
 
+// Decode grid: as many workgroups as the device keeps resident at once (so the static split of
+// the items over the waves is also a split over time), but no more than there can be items.
+template <typename E, int D, int NB>
+int launch_partials_nb(const AttnParams& a, hipStream_t s) {
+  static int per_cu_cache[64];   // resident workgroups per CU, per device (benign race)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  int per_cu = (dev >= 0 && dev < 64) ? per_cu_cache[dev] : 0;
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<E, D, NB>, kThreads, 0) !=
+            hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    (void)hipGetLastError();
+    if (dev >= 0 && dev < 64) per_cu_cache[dev] = per_cu;
+  }
+  const int64_t items_max = (int64_t)a.batch * a.hkv * a.jmax;
+  int64_t wgs = std::min<int64_t>((int64_t)cu_count() * per_cu, (items_max + kWaves - 1) / kWaves);
+  wgs = std::max<int64_t>(wgs, (a.hkv + kWaves - 1) / kWaves);   // at least one wave per KV head
+  hipLaunchKernelGGL((decode_split_kernel<E, D, NB>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+  return launched();
+}
+
 template <typename E, int D>
 int launch_partials(const AttnParams& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.jmax + kWaves - 1) / kWaves), (unsigned)a.hkv, (unsigned)a.batch);
-  if (a.group <= 16) hipLaunchKernelGGL((decode_split_kernel<E, D, 1>), grid, dim3(kThreads), 0, s, a);
-  else if (a.group == 32) hipLaunchKernelGGL((decode_split_kernel<E, D, 2>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((decode_split_kernel<E, D, 4>), grid, dim3(kThreads), 0, s, a);
-  return launched();
+  if (a.group <= 16) return launch_partials_nb<E, D, 1>(a, s);
+  if (a.group == 32) return launch_partials_nb<E, D, 2>(a, s);
+  return launch_partials_nb<E, D, 4>(a, s);
 }
 
 int launch_combine(const AttnParams& a, int D, hipStream_t s) {
