@@ -128,8 +128,9 @@ int bi_attn_decode(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
  * them in ascending split order on the row's owner), and for per-kernel timing.
  * bi_attn_decode(...) == bi_attn_decode_partials(...) then bi_attn_decode_combine(...) on
  * the same stream, with the same cfg, seq_lens, batch, max_seq_len and workspace, bit for bit.
- * Partials layout in the workspace (fp32): first (m, l) pairs [batch*Hq][Jmax], padded to
- * 256 bytes, then accumulators [batch*Hq][Jmax][D]; Jmax = ceil(max_seq_len / S) for
+ * Partials layout in the workspace (fp32), G = Hq / Hkv: first (m, l) pairs
+ * [batch*Hkv][Jmax][G], padded to 256 bytes, then accumulators [batch*Hkv][Jmax][G][D]; query
+ * head h of sequence b is entry (b*Hkv + h/G, j, h%G). Jmax = ceil(max_seq_len / S) for
  * BI_SPLIT_FIXED. m is in base-2 units (max of q.k * scale * log2(e)).
  */
 int bi_attn_decode_partials(const bi_attn_cfg* cfg, const void* q, const void* k_cache,

@@ -32,8 +32,8 @@ struct AttnParams {
   const int32_t* seq_lens;
   const int32_t* q_starts;   // prefill only
   float* out;
-  float* ws_acc;             // decode: [rows][jmax][D]
-  float2* ws_ml;             // decode: [rows][jmax]  (m, l)
+  float* ws_acc;             // decode: [batch Hkv][jmax][group][D]
+  float2* ws_ml;             // decode: [batch Hkv][jmax][group]  (m, l)
   int32_t max_pages, num_pages, batch, total_tokens, max_q_len, max_seq_len;
   int32_t hq, hkv, group, split, policy, num_cus, jmax;
   float cscale;              // softmax scale * log2(e)
@@ -50,11 +50,24 @@ __device__ __forceinline__ int split_len(const AttnParams& a, int len) {
   return max(32, (s + 31) / 32 * 32);
 }
 
+// Index of the partial of split j of query row `row` (= b Hq + h) in the workspace: the rows of
+// one (sequence, KV head) are adjacent for each split, so one split's partials are contiguous.
+__device__ __forceinline__ size_t part_index(const AttnParams& a, size_t row, int j) {
+  return (row / a.group * a.jmax + j) * a.group + row % a.group;
+}
+
 // Physical page of logical page `lp` of sequence b, or -1 when it must not be read.
 __device__ __forceinline__ int page_of(const AttnParams& a, int b, int lp, int seq_len) {
   if (lp < 0 || lp >= a.max_pages || lp * kPage >= seq_len) return -1;
   const int p = a.page_table[(size_t)b * a.max_pages + lp];
   return (p >= 0 && p < a.num_pages) ? p : -1;
+}
+// The same without a branch around the load (an out-of-range lp reads entry 0 of row b,
+// which exists, and discards it), for code that keeps other loads in flight meanwhile.
+__device__ __forceinline__ int page_of_nb(const AttnParams& a, int b, int lp, int seq_len) {
+  const bool ok = lp >= 0 && lp < a.max_pages && lp * kPage < seq_len;
+  const int p = a.page_table[(size_t)b * a.max_pages + (ok ? lp : 0)];
+  return (ok && p >= 0 && p < a.num_pages) ? p : -1;
 }
 
 // Rows read in place of a page that must not be dereferenced (table entry absent, outside the
@@ -157,109 +170,164 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   // loads of the next sub-tile stay in flight while the current one is computed.
   const char* nan_rows = (const char*)&kNanRows;
   const char* zero_rows = (const char*)kZeroRows;
-  struct Buf {
-    KOp k[2][NKS];
-    VRow v[8];
+
+  // A unit is up to 32 sub-tiles of one split (a window of 64 pages, one page id per lane).
+  // The loads of a unit's first sub-tile are issued while the previous unit's last sub-tile is
+  // computed, so the stream of loads does not stop between splits.
+  struct Unit {
+    int b, j, w0, seq_len, k_begin, nsub, nw;
   };
-
-  for (int it = 0; it < n_items; ++it) {
-    const int seq_len = __builtin_amdgcn_readlane(len_v, b - cb);
-    const int pos = seq_len - 1;
-    const int S = split_len(a, seq_len);
-    const int k_begin = j * S;
-    const int k_end = min(k_begin + S, seq_len);
-    const int nsub = (k_end - k_begin + kSubTile - 1) / kSubTile;
-    const int lp0 = k_begin / kPage;
-
-    typename F::Q qf[NB];
-    RowState<D> st[NB];
-    int posv[NB];
-#pragma unroll
-    for (int cq = 0; cq < NB; ++cq) {
-      posv[cq] = pos;
-      const int hl = cq * 16 + c;   // head within the group
-      const char* row = hl < a.group ? a.q + ((size_t)b * a.hq + kvh * a.group + hl) * (size_t)ROWB
-                                     : zero_rows;
-      F::load_q(qf[cq], row, g);
+  auto make_unit = [&](int ub, int uj, int w0, int len) {
+    Unit u;
+    u.b = ub;
+    u.j = uj;
+    u.w0 = w0;
+    u.seq_len = len;
+    const int S = split_len(a, len);
+    u.k_begin = uj * S;
+    u.nsub = (min(u.k_begin + S, len) - u.k_begin + kSubTile - 1) / kSubTile;
+    u.nw = min(32, u.nsub - w0);
+    return u;
+  };
+  int items_done = 0;
+  // the unit after u: the next window of its split, else window 0 of the next split
+  auto next_unit = [&](const Unit& u, Unit& un) {
+    if (u.w0 + 32 < u.nsub) {
+      un = make_unit(u.b, u.j, u.w0 + 32, u.seq_len);
+      return true;
     }
-
-    auto compute = [&](Buf& buf, int t) {
-      const int key0 = k_begin + kSubTile * t;
-      if (key0 + kSubTile > seq_len) {
-        // stale slots past the sequence end: V rows become zero, scores are masked below
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (key0 + F::vkey(i, g) >= seq_len) buf.v[i] = F::zero_v();
-      }
-      auto getK = [&](int kb, int s2) { return buf.k[kb][s2]; };
-      auto getV = [&](int x) {
-        if constexpr (std::is_same<E, float>::value) return buf.v[x];
-        else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
-      };
-      subtile_step<E, D, NB, false>(st, qf, posv, getK, getV, a.cscale, key0, g, t == 0,
-                                    key0 + kSubTile - 1 > pos);
-    };
-
-    // Windows of 32 sub-tiles: the window's 64 physical page ids, one per lane.
-    for (int w0 = 0; w0 < nsub; w0 += 32) {
-      const int nw = min(32, nsub - w0);
-      const int pg = page_of(a, b, lp0 + 2 * w0 + lane, seq_len);
-      // sub-tile t of the window; t >= nw (the loads issued past the end) reads the stand-ins
-      auto fetch = [&](Buf& buf, int t) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int pl = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
-          const int page = t < nw ? pl : -1;
-          const char* kp = page >= 0 ? kbase + (size_t)page * page_stride : nan_rows;
-          const char* vp = page >= 0 ? vbase + (size_t)page * page_stride : zero_rows;
-#pragma unroll
-          for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
-#pragma unroll
-          for (int i = 4 * kb; i < 4 * kb + 4; ++i)
-            buf.v[i] = F::v_row(vp + (F::vkey(i, g) - 16 * kb) * ROWB, c);
-        }
-      };
-      Buf b0, b1;
-      fetch(b0, 0);
-      for (int t = 0; t < nw; t += 2) {
-        fetch(b1, t + 1);
-        compute(b0, w0 + t);
-        if (t + 1 >= nw) break;
-        fetch(b0, t + 2);
-        compute(b1, w0 + t + 1);
-      }
-    }
-
-    // Partial of split j for every real head of the block.
-#pragma unroll
-    for (int cq = 0; cq < NB; ++cq) {
-      const int hl = cq * 16 + c;
-      if (hl >= a.group) continue;
-      const size_t row = (size_t)b * a.hq + kvh * a.group + hl;
-      const size_t pidx = row * a.jmax + j;
-      float* dst = a.ws_acc + pidx * D + 4 * g * NM;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int mb = 0; mb < NM; mb += 4) {
-          f32x4 v = {st[cq].acc[mb][r], st[cq].acc[mb + 1][r], st[cq].acc[mb + 2][r], st[cq].acc[mb + 3][r]};
-          *(f32x4*)(dst + r * NM + mb) = v;
-        }
-      if (g == 0) a.ws_ml[pidx] = make_float2(st[cq].m, st[cq].l);
-    }
-
-    // next item: the next split of this sequence, else split 0 of the next sequence with splits
-    if (++j >= __builtin_amdgcn_readlane(nj_v, b - cb)) {
-      j = 0;
+    if (items_done + 1 >= n_items) return false;
+    int nb2 = u.b, nj2 = u.j + 1;
+    if (nj2 >= __builtin_amdgcn_readlane(nj_v, nb2 - cb)) {
+      nj2 = 0;
       do {
-        ++b;
-        if (b - cb >= 64) {
+        ++nb2;
+        if (nb2 - cb >= 64) {
           cb += 64;
           len_v = chunk_len(cb);
           nj_v = splits_of(len_v);
         }
-      } while (b < a.batch && __builtin_amdgcn_readlane(nj_v, b - cb) == 0);
+      } while (nb2 < a.batch && __builtin_amdgcn_readlane(nj_v, nb2 - cb) == 0);
     }
+    un = make_unit(nb2, nj2, 0, __builtin_amdgcn_readlane(len_v, nb2 - cb));
+    return true;
+  };
+  auto unit_pages = [&](const Unit& u) {
+    return page_of_nb(a, u.b, u.k_begin / kPage + 2 * u.w0 + lane, u.seq_len);
+  };
+  auto load_q_of = [&](typename F::Q (&qq)[NB], int qb, bool real) {
+#pragma unroll
+    for (int cq = 0; cq < NB; ++cq) {
+      const int hl = cq * 16 + c;   // head within the group
+      const char* row = real && hl < a.group
+                            ? a.q + ((size_t)qb * a.hq + kvh * a.group + hl) * (size_t)ROWB
+                            : zero_rows;
+      F::load_q(qq[cq], row, g);
+    }
+  };
+
+  struct Buf {
+    KOp k[2][NKS];
+    VRow v[8];
+  };
+  // per wave: one split's accumulators [NB 16 rows][D], staged for contiguous stores (only
+  // this wave touches its slice, and one wave's LDS accesses complete in order)
+  __shared__ __attribute__((aligned(16))) float lds_part_all[kWaves][NB * 16 * D];
+  float* lds_part = lds_part_all[threadIdx.x >> 6];
+  Unit u = make_unit(b, j, 0, __builtin_amdgcn_readlane(len_v, b - cb)), un;
+  int pg = unit_pages(u), pgn = -1;
+  typename F::Q qf[NB], qn[NB];
+  load_q_of(qf, u.b, true);
+  RowState<D> st[NB];
+  bool has_next = false;
+  // sub-tile t of unit u; t == u.nw is sub-tile 0 of the next unit when `next`, else (and when
+  // there is none) the stand-ins
+  auto fetch = [&](Buf& buf, int t, bool next) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int pc = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
+      const int pn = __builtin_amdgcn_readlane(pgn, kb);
+      const int page = t < u.nw ? pc : (next && has_next ? pn : -1);
+      const char* kp = page >= 0 ? kbase + (size_t)page * page_stride : nan_rows;
+      const char* vp = page >= 0 ? vbase + (size_t)page * page_stride : zero_rows;
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
+#pragma unroll
+      for (int i = 4 * kb; i < 4 * kb + 4; ++i)
+        buf.v[i] = F::v_row(vp + (F::vkey(i, g) - 16 * kb) * ROWB, c);
+    }
+  };
+  auto compute = [&](Buf& buf, int t) {
+    const int key0 = u.k_begin + kSubTile * (u.w0 + t);
+    const int pos = u.seq_len - 1;
+    if (key0 + kSubTile > u.seq_len) {
+      // stale slots past the sequence end: V rows become zero, scores are masked below
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (key0 + F::vkey(i, g) >= u.seq_len) buf.v[i] = F::zero_v();
+    }
+    int posv[NB];
+#pragma unroll
+    for (int cq = 0; cq < NB; ++cq) posv[cq] = pos;
+    auto getK = [&](int kb, int s2) { return buf.k[kb][s2]; };
+    auto getV = [&](int x) {
+      if constexpr (std::is_same<E, float>::value) return buf.v[x];
+      else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
+    };
+    subtile_step<E, D, NB, false>(st, qf, posv, getK, getV, a.cscale, key0, g, u.w0 + t == 0,
+                                  key0 + kSubTile - 1 > pos);
+  };
+  // Every sub-tile of unit u, its first one already in flight in b0. Even sub-tiles are
+  // computed from b0 and odd ones from b1; the next unit's first sub-tile goes to b0, during
+  // the last compute when that is from b1 (an even count), else right after it.
+  Buf b0, b1;
+  auto run = [&]() {
+    for (int t = 0;; t += 2) {
+      fetch(b1, t + 1, false);
+      compute(b0, t);
+      if (t + 1 >= u.nw) {
+        fetch(b0, t + 1, true);
+        return;
+      }
+      fetch(b0, t + 2, true);
+      compute(b1, t + 1);
+      if (t + 2 >= u.nw) return;
+    }
+  };
+
+  fetch(b0, 0, false);
+  for (;;) {
+    has_next = next_unit(u, un);
+    pgn = has_next ? unit_pages(un) : -1;
+    load_q_of(qn, un.b, has_next);
+    run();
+    if (u.w0 + u.nw >= u.nsub) {
+      // Partial of split u.j: the accumulators of the group's heads are one contiguous block
+      // of the workspace, written through the wave's LDS slice in whole 1 KB stores (each lane
+      // holds 4 NM scattered-by-row values; stored directly they would be 16-byte pieces).
+#pragma unroll
+      for (int cq = 0; cq < NB; ++cq) {
+        float* lrow = lds_part + (cq * 16 + c) * D + 4 * g * NM;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int mb = 0; mb < NM; mb += 4)
+            *(f32x4*)(lrow + r * NM + mb) = f32x4{st[cq].acc[mb][r], st[cq].acc[mb + 1][r],
+                                                  st[cq].acc[mb + 2][r], st[cq].acc[mb + 3][r]};
+        const int hl = cq * 16 + c;
+        if (g == 0 && hl < a.group)
+          a.ws_ml[part_index(a, (size_t)u.b * a.hq + kvh * a.group + hl, u.j)] =
+              make_float2(st[cq].m, st[cq].l);
+      }
+      float* dst = a.ws_acc + part_index(a, (size_t)u.b * a.hq + kvh * a.group, u.j) * D;
+      for (int i = lane; i < a.group * (D / 4); i += 64) *(f32x4*)(dst + 4 * i) = *(const f32x4*)(lds_part + 4 * i);
+      ++items_done;
+    }
+    if (!has_next) break;
+    u = un;
+    pg = pgn;
+#pragma unroll
+    for (int cq = 0; cq < NB; ++cq) qf[cq] = qn[cq];
   }
 }
 
@@ -280,8 +348,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
   }
   const int S = split_len(a, seq_len);
   const int J = (seq_len - 1) / S + 1;
-  const float2* ml = a.ws_ml + row * a.jmax;
-  const float* acc = a.ws_acc + row * a.jmax * D + lane * PER;
+  const float2* ml = a.ws_ml + part_index(a, row, 0);
+  const float* acc = a.ws_acc + part_index(a, row, 0) * D + lane * PER;
+  const size_t jstride = a.group;   // partials of consecutive splits of one row
   float M = 0.f, L = 0.f, A[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) A[e] = 0.f;
@@ -292,9 +361,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < J) {
-        mlj[u] = ml[j0 + u];
+        mlj[u] = ml[(size_t)(j0 + u) * jstride];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) accj[u][e] = acc[(size_t)(j0 + u) * D + e];
+        for (int e = 0; e < PER; ++e) accj[u][e] = acc[(size_t)(j0 + u) * jstride * D + e];
       }
     }
 #pragma unroll
