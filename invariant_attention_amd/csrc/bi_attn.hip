@@ -94,9 +94,9 @@ __device__ __forceinline__ const char* kv_row(const char* cache, const AttnParam
 
 // ------------------------------------------------------------------------------------------
 // Decode. The work items of a KV head are the splits (b, j) of every sequence, in ascending b
-// and then j. The grid holds as many waves as the device keeps resident; wave w of a head takes
-// the k = ceil(items / waves) consecutive items from w k, so every launched wave has work (no
-// workgroup exits at once) and all of them finish after about k items. Per item, operands
+// and then j. The grid holds as many waves as the device keeps resident; of W waves per head,
+// wave w takes items w, w + W, w + 2W, ..., so every resident wave (and so every CU) gets the
+// same share of the work, within one item, and no workgroup exits at once. Per item, operands
 // stream from HBM straight into MFMA registers with two sub-tiles in flight: the loads of
 // sub-tile t+1 are issued before sub-tile t is computed.
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -140,26 +140,29 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   int total = 0;
   for (int cb = 0; cb < a.batch; cb += 64) total += wave_sum_i(splits_of(chunk_len(cb)));
   total = __builtin_amdgcn_readfirstlane(total);
-  const int k = (total + W - 1) / W;
-  const int i0 = w * k;
-  if (i0 >= total) return;
-  const int n_items = min(k, total - i0);
-  // item i0: sequence b, split j
-  int cb = 0, before = 0, len_v = 0, nj_v = 0, b = 0, j = 0;
-  for (;;) {
-    len_v = chunk_len(cb);
-    nj_v = splits_of(len_v);
-    const int incl = wave_incl_scan(nj_v, lane);
-    const int tot = __builtin_amdgcn_readlane(incl, 63);
-    if (before + tot > i0) {
-      const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before + incl <= i0));
-      b = cb + nb;
-      j = i0 - before - (nb > 0 ? __builtin_amdgcn_readlane(incl, nb - 1) : 0);
-      break;
+  if (w >= total) return;
+  // Item i -> (sequence, split), for increasing i: a cursor over the chunks of 64 sequences
+  // (inclusive prefix sums of their split counts in incl_v; `before` items precede the chunk).
+  int cb = 0, before = 0;
+  int len_v = chunk_len(0);
+  int nj_v = splits_of(len_v);
+  int incl_v = wave_incl_scan(nj_v, lane);
+  auto locate = [&](int i, int& ob, int& oj) {
+    for (;;) {
+      const int tot = __builtin_amdgcn_readlane(incl_v, 63);
+      if (before + tot > i) break;
+      before += tot;
+      cb += 64;
+      len_v = chunk_len(cb);
+      nj_v = splits_of(len_v);
+      incl_v = wave_incl_scan(nj_v, lane);
     }
-    before += tot;
-    cb += 64;
-  }
+    const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before + incl_v <= i));
+    ob = cb + nb;
+    oj = i - before - (nb > 0 ? __builtin_amdgcn_readlane(incl_v, nb - 1) : 0);
+  };
+  int item = w, b = 0, j = 0;
+  locate(item, b, j);
 
   const size_t head_stride = (size_t)kPage * ROWB;
   const size_t page_stride = (size_t)a.hkv * head_stride;
@@ -189,26 +192,16 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
     u.nw = min(32, u.nsub - w0);
     return u;
   };
-  int items_done = 0;
-  // the unit after u: the next window of its split, else window 0 of the next split
+  // the unit after u: the next window of its split, else window 0 of the wave's next item
   auto next_unit = [&](const Unit& u, Unit& un) {
     if (u.w0 + 32 < u.nsub) {
       un = make_unit(u.b, u.j, u.w0 + 32, u.seq_len);
       return true;
     }
-    if (items_done + 1 >= n_items) return false;
-    int nb2 = u.b, nj2 = u.j + 1;
-    if (nj2 >= __builtin_amdgcn_readlane(nj_v, nb2 - cb)) {
-      nj2 = 0;
-      do {
-        ++nb2;
-        if (nb2 - cb >= 64) {
-          cb += 64;
-          len_v = chunk_len(cb);
-          nj_v = splits_of(len_v);
-        }
-      } while (nb2 < a.batch && __builtin_amdgcn_readlane(nj_v, nb2 - cb) == 0);
-    }
+    if (item + W >= total) return false;
+    item += W;
+    int nb2, nj2;
+    locate(item, nb2, nj2);
     un = make_unit(nb2, nj2, 0, __builtin_amdgcn_readlane(len_v, nb2 - cb));
     return true;
   };
@@ -236,7 +229,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   float* lds_part = lds_part_all[threadIdx.x >> 6];
   Unit u = make_unit(b, j, 0, __builtin_amdgcn_readlane(len_v, b - cb)), un;
   int pg = unit_pages(u), pgn = -1;
-  typename F::Q qf[NB], qn[NB];
+  typename F::Q qf[NB];
   load_q_of(qf, u.b, true);
   RowState<D> st[NB];
   bool has_next = false;
@@ -299,8 +292,10 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   for (;;) {
     has_next = next_unit(u, un);
     pgn = has_next ? unit_pages(un) : -1;
-    load_q_of(qn, un.b, has_next);
     run();
+    // q of the next unit, into registers the last compute no longer needs (its latency overlaps
+    // the partial's stores; the next unit's first loads are already in flight)
+    if (has_next && un.b != u.b) load_q_of(qf, un.b, true);
     if (u.w0 + u.nw >= u.nsub) {
       // Partial of split u.j: the accumulators of the group's heads are one contiguous block
       // of the workspace, written through the wave's LDS slice in whole 1 KB stores (each lane
@@ -321,64 +316,63 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
       }
       float* dst = a.ws_acc + part_index(a, (size_t)u.b * a.hq + kvh * a.group, u.j) * D;
       for (int i = lane; i < a.group * (D / 4); i += 64) *(f32x4*)(dst + 4 * i) = *(const f32x4*)(lds_part + 4 * i);
-      ++items_done;
     }
     if (!has_next) break;
     u = un;
     pg = pgn;
-#pragma unroll
-    for (int cq = 0; cq < NB; ++cq) qf[cq] = qn[cq];
   }
 }
 
-// Combine: one wave per (token, q head); lane t owns dims t * D/64 ... in ascending j.
+// Combine. The partials of one (sequence, KV head) and split are a contiguous [group][D] block;
+// a wave owns 256 consecutive floats of that block (lane: 4 floats of one row), folds them over
+// the splits in ascending j and writes A / L. Loads of kCombU splits are issued together.
+constexpr int kCombU = 8;
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
-  constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
-  const size_t row = (size_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= (size_t)a.batch * a.hq) return;
-  const int b = (int)(row / a.hq);
+  const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
+  const int G = a.group;
+  const int chunks = (G * D + 255) / 256;              // waves per (sequence, KV head)
+  const int rg = gw / chunks, q = gw - rg * chunks;   // rg = b Hkv + kvh
+  if (rg >= a.batch * a.hkv) return;
+  const int b = rg / a.hkv;
+  const int f = 256 * q + 4 * lane;                   // float of the [G][D] block
+  if (f >= G * D) return;
+  const int hl = f / D, d0 = f - hl * D;
+  float* o = a.out + ((size_t)rg * G + hl) * D + d0;   // row b Hq + kvh G + hl
   const int seq_len = a.seq_lens[b];
-  float* o = a.out + row * D + lane * PER;
   if (seq_len <= 0 || seq_len > a.max_seq_len) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = __builtin_nanf("");
+    *(f32x4*)o = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     return;
   }
-  const int S = split_len(a, seq_len);
-  const int J = (seq_len - 1) / S + 1;
-  const float2* ml = a.ws_ml + part_index(a, row, 0);
-  const float* acc = a.ws_acc + part_index(a, row, 0) * D + lane * PER;
-  const size_t jstride = a.group;   // partials of consecutive splits of one row
-  float M = 0.f, L = 0.f, A[PER];
+  const int J = (seq_len - 1) / split_len(a, seq_len) + 1;
+  const size_t blk0 = (size_t)rg * a.jmax * G;        // split 0 of the row group
+  const float2* ml = a.ws_ml + blk0 + hl;
+  const float* acc = a.ws_acc + blk0 * D + f;
+  const size_t ml_step = G, acc_step = (size_t)G * D;
+  float M = 0.f, L = 0.f;
+  f32x4 A = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < J; j0 += kCombU) {
+    float2 mlj[kCombU];
+    f32x4 accj[kCombU];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) A[e] = 0.f;
-  constexpr int U = 8;
-  for (int j0 = 0; j0 < J; j0 += U) {
-    float2 mlj[U];
-    float accj[U][PER];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (j0 + u < J) {
-        mlj[u] = ml[(size_t)(j0 + u) * jstride];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) accj[u][e] = acc[(size_t)(j0 + u) * jstride * D + e];
-      }
+    for (int u = 0; u < kCombU; ++u) {
+      const int jj = min(j0 + u, J - 1);              // in range; the extra ones are not folded
+      mlj[u] = ml[jj * ml_step];
+      accj[u] = *(const f32x4*)(acc + jj * acc_step);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kCombU; ++u) {
       if (j0 + u < J) {
         const bool first = (j0 + u) == 0;
         float fa, fb;
         fold_scalars(M, L, mlj[u].x, mlj[u].y, first, fa, fb);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) A[e] = fold_elem(A[e], accj[u][e], fa, fb, first);
+        for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], accj[u][e], fa, fb, first);
       }
     }
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = A[e] / L;
+  *(f32x4*)o = f32x4{A[0] / L, A[1] / L, A[2] / L, A[3] / L};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -609,7 +603,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Page update: one thread per 16-byte chunk of a (token, KV head) row of K or V.
+// Page update: one wave per new token. The wave finds the token's sequence with one ballot per
+// 64 sequences (the count of q_starts[b] <= t; q_starts ascending), then copies the token's K
+// and V rows of every KV head into its page slot, 16 bytes per lane.
 template <int ROWB>
 __global__ __launch_bounds__(256) void page_update_kernel(const char* k_new, const char* v_new,
                                                           const int32_t* q_starts,
@@ -619,34 +615,34 @@ __global__ __launch_bounds__(256) void page_update_kernel(const char* k_new, con
                                                           int total_tokens, int hkv,
                                                           char* k_cache, char* v_cache) {
   constexpr int CH = ROWB / 16;
-  const size_t n = (size_t)total_tokens * hkv * CH * 2;
-  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-       idx += (size_t)gridDim.x * blockDim.x) {
-    const int which = (int)(idx % 2);
-    const size_t rest = idx / 2;
-    const int ch = (int)(rest % CH);
-    const size_t th = rest / CH;
-    const int h = (int)(th % hkv);
-    const int t = (int)(th / hkv);
-    // sequence of token t: last b with q_starts[b] <= t
-    int lo = 0, hi = batch;                       // invariant: q_starts[lo] <= t < q_starts[hi]
-    if (t < q_starts[0] || t >= q_starts[batch]) continue;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (q_starts[mid] <= t) lo = mid; else hi = mid;
+  const int lane = threadIdx.x & 63;
+  const int t0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int first = q_starts[0], end = q_starts[batch];
+  for (int t = t0; t < total_tokens; t += (int)gridDim.x * 4) {
+    if (t < first || t >= end) continue;
+    int cnt = 0;
+    for (int c0 = 0; c0 < batch; c0 += 64) {
+      const int i = c0 + lane;
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < batch && q_starts[i] <= t));
     }
-    const int bq = lo;
-    const int n_new = q_starts[bq + 1] - q_starts[bq];
-    const int pos = seq_lens[bq] - n_new + (t - q_starts[bq]);
+    const int bq = cnt - 1;                         // last b with q_starts[b] <= t
+    const int s0 = q_starts[bq], s1 = q_starts[bq + 1];
+    if (t >= s1) continue;                          // q_starts not ascending: not a token of bq
+    const int pos = seq_lens[bq] - (s1 - s0) + (t - s0);
     if (pos < 0) continue;
     const int lp = pos / kPage;
     if (lp >= max_pages) continue;
     const int page = page_table[(size_t)bq * max_pages + lp];
     if (page < 0 || page >= num_pages) continue;
-    const size_t src = ((size_t)t * hkv + h) * ROWB + ch * 16;
-    const size_t dst = (((size_t)page * hkv + h) * kPage + (pos % kPage)) * ROWB + ch * 16;
-    if (which == 0) *(u32x4*)(k_cache + dst) = *(const u32x4*)(k_new + src);
-    else *(u32x4*)(v_cache + dst) = *(const u32x4*)(v_new + src);
+    for (int i = lane; i < hkv * CH; i += 64) {
+      const int h = i / CH, ch = i - h * CH;
+      const size_t src = ((size_t)t * hkv + h) * ROWB + ch * 16;
+      const size_t dst = (((size_t)page * hkv + h) * kPage + (pos % kPage)) * ROWB + ch * 16;
+      const u32x4 kv = *(const u32x4*)(k_new + src);
+      const u32x4 vv = *(const u32x4*)(v_new + src);
+      *(u32x4*)(k_cache + dst) = kv;
+      *(u32x4*)(v_cache + dst) = vv;
+    }
   }
 }
 
@@ -755,8 +751,8 @@ int launch_partials(const AttnParams& a, hipStream_t s) {
 }
 
 int launch_combine(const AttnParams& a, int D, hipStream_t s) {
-  const unsigned rows = (unsigned)((int64_t)a.batch * a.hq);
-  const dim3 grid((rows + kWaves - 1) / kWaves);
+  const int64_t waves = (int64_t)a.batch * a.hkv * ((a.group * D + 255) / 256);
+  const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
   if (D == 128) hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(kThreads), 0, s, a);
   return launched();
@@ -856,8 +852,8 @@ int bi_kv_page_update(const bi_attn_cfg* cfg, const void* k_new, const void* v_n
   if (max_pages == 0 || num_pages == 0) return BI_EINVAL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return BI_EINVAL;
   const int rowb = cfg->head_dim * (cfg->dtype == BI_BF16 ? 2 : 4);
-  const size_t work = (size_t)total_tokens * cfg->num_kv_heads * (rowb / 16) * 2;
-  const unsigned blocks = (unsigned)((work + 255) / 256 < 65536 ? (work + 255) / 256 : 65536);
+  const int64_t waves = std::min<int64_t>(total_tokens, 65536);   // one wave per token (strided)
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
 #define BI_PU(RB)                                                                                 \
   hipLaunchKernelGGL((page_update_kernel<RB>), dim3(blocks), dim3(256), 0, stream,               \
                      (const char*)k_new, (const char*)v_new, q_starts, seq_lens, page_table,      \
