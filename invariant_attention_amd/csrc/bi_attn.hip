@@ -325,8 +325,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
 
 // Combine. The partials of one (sequence, KV head) and split are a contiguous [group][D] block;
 // a wave owns 256 consecutive floats of that block (lane: 4 floats of one row), folds them over
-// the splits in ascending j and writes A / L. Loads of kCombU splits are issued together.
-constexpr int kCombU = 8;
+// the splits in ascending j and writes A / L. Loads of kCombU splits are issued together, the
+// first ones before the row's split count is known.
+constexpr int kCombU = 16;
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
   const int lane = threadIdx.x & 63;
@@ -340,26 +341,36 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
   if (f >= G * D) return;
   const int hl = f / D, d0 = f - hl * D;
   float* o = a.out + ((size_t)rg * G + hl) * D + d0;   // row b Hq + kvh G + hl
+  const size_t blk0 = (size_t)rg * a.jmax * G;        // split 0 of the row group
+  const float2* ml = a.ws_ml + blk0 + hl;
+  const float* acc = a.ws_acc + blk0 * D + f;
+  const size_t ml_step = G, acc_step = (size_t)G * D;
+  // the first kCombU splits' loads go out with the length's (the workspace holds jmax splits;
+  // those past the row's own count are read but not folded)
   const int seq_len = a.seq_lens[b];
+  float2 mlj[kCombU];
+  f32x4 accj[kCombU];
+#pragma unroll
+  for (int u = 0; u < kCombU; ++u) {
+    const int jj = min(u, a.jmax - 1);
+    mlj[u] = ml[jj * ml_step];
+    accj[u] = *(const f32x4*)(acc + jj * acc_step);
+  }
   if (seq_len <= 0 || seq_len > a.max_seq_len) {
     *(f32x4*)o = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     return;
   }
   const int J = (seq_len - 1) / split_len(a, seq_len) + 1;
-  const size_t blk0 = (size_t)rg * a.jmax * G;        // split 0 of the row group
-  const float2* ml = a.ws_ml + blk0 + hl;
-  const float* acc = a.ws_acc + blk0 * D + f;
-  const size_t ml_step = G, acc_step = (size_t)G * D;
   float M = 0.f, L = 0.f;
   f32x4 A = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < J; j0 += kCombU) {
-    float2 mlj[kCombU];
-    f32x4 accj[kCombU];
+    if (j0 > 0) {
 #pragma unroll
-    for (int u = 0; u < kCombU; ++u) {
-      const int jj = min(j0 + u, J - 1);              // in range; the extra ones are not folded
-      mlj[u] = ml[jj * ml_step];
-      accj[u] = *(const f32x4*)(acc + jj * acc_step);
+      for (int u = 0; u < kCombU; ++u) {
+        const int jj = min(j0 + u, J - 1);            // in range; the extra ones are not folded
+        mlj[u] = ml[jj * ml_step];
+        accj[u] = *(const f32x4*)(acc + jj * acc_step);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
@@ -620,6 +631,12 @@ __global__ __launch_bounds__(256) void page_update_kernel(const char* k_new, con
   const int first = q_starts[0], end = q_starts[batch];
   for (int t = t0; t < total_tokens; t += (int)gridDim.x * 4) {
     if (t < first || t >= end) continue;
+    // the token's first 64 chunks are loaded before its page is known
+    const bool l0 = lane < hkv * CH;
+    const int h0 = lane / CH, ch0 = lane - h0 * CH;
+    const size_t src0 = ((size_t)t * hkv + (l0 ? h0 : 0)) * ROWB + (l0 ? ch0 : 0) * 16;
+    const u32x4 k0 = *(const u32x4*)(k_new + src0);
+    const u32x4 v0 = *(const u32x4*)(v_new + src0);
     int cnt = 0;
     for (int c0 = 0; c0 < batch; c0 += 64) {
       const int i = c0 + lane;
@@ -634,10 +651,16 @@ __global__ __launch_bounds__(256) void page_update_kernel(const char* k_new, con
     if (lp >= max_pages) continue;
     const int page = page_table[(size_t)bq * max_pages + lp];
     if (page < 0 || page >= num_pages) continue;
-    for (int i = lane; i < hkv * CH; i += 64) {
+    const size_t slot = ((size_t)page * hkv * kPage + (pos % kPage)) * ROWB;   // head 0 row
+    if (l0) {
+      const size_t dst = slot + (size_t)h0 * kPage * ROWB + ch0 * 16;
+      *(u32x4*)(k_cache + dst) = k0;
+      *(u32x4*)(v_cache + dst) = v0;
+    }
+    for (int i = lane + 64; i < hkv * CH; i += 64) {
       const int h = i / CH, ch = i - h * CH;
       const size_t src = ((size_t)t * hkv + h) * ROWB + ch * 16;
-      const size_t dst = (((size_t)page * hkv + h) * kPage + (pos % kPage)) * ROWB + ch * 16;
+      const size_t dst = slot + (size_t)h * kPage * ROWB + ch * 16;
       const u32x4 kv = *(const u32x4*)(k_new + src);
       const u32x4 vv = *(const u32x4*)(v_new + src);
       *(u32x4*)(k_cache + dst) = kv;
