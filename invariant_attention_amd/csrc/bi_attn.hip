@@ -310,9 +310,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
             *(f32x4*)(lrow + r * NM + mb) = f32x4{st[cq].acc[mb][r], st[cq].acc[mb + 1][r],
                                                   st[cq].acc[mb + 2][r], st[cq].acc[mb + 3][r]};
         const int hl = cq * 16 + c;
+        const float rl = row_l(st[cq]);
         if (g == 0 && hl < a.group)
-          a.ws_ml[part_index(a, (size_t)u.b * a.hq + kvh * a.group + hl, u.j)] =
-              make_float2(st[cq].m, st[cq].l);
+          a.ws_ml[part_index(a, (size_t)u.b * a.hq + kvh * a.group + hl, u.j)] = make_float2(st[cq].m, rl);
       }
       float* dst = a.ws_acc + part_index(a, (size_t)u.b * a.hq + kvh * a.group, u.j) * D;
       for (int i = lane; i < a.group * (D / 4); i += 64) *(f32x4*)(dst + 4 * i) = *(const f32x4*)(lds_part + 4 * i);
@@ -390,9 +390,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
 // Prefill: a workgroup owns a tile of query columns (token-major: column = token * G + head)
 // of one (sequence, KV head) and walks every 32-key sub-tile that any of its rows needs, in
 // ascending order, folding each finished split into the row state. K/V sub-tiles are staged
-// in LDS and shared by all NW waves (the global loads of sub-tile u+1 are in flight while u
-// is computed); each wave holds NBW column blocks. The row accumulator A, touched only when
-// a split ends, lives in LDS next to the sequence's cached page ids. For bf16 the PV operand
+// in LDS and shared by all NW waves (the global loads of the next NPF sub-tiles are in flight
+// while one is computed); each wave holds NBW column blocks. The row accumulator A, touched
+// only when a split ends, lives in registers (AREG) or in LDS. For bf16 the PV operand
 // comes from the row-major V sub-tile through transposing LDS reads, which puts head dim
 // d = 16 mb + 4 g + r in accumulator (mb, r) of lane group g; for fp32 the layout is the
 // decode one, d = NM (4 g + r) + mb.
@@ -403,8 +403,8 @@ template <int D, typename E> struct Lds {
 };
 constexpr int kPageCache = 2048;
 
-template <typename E, int D, int NBW, int NW, bool LANESEL, bool RING>
-__global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
+template <typename E, int D, int NBW, int NW, bool LANESEL, bool RING, int NPF, bool AREG, int MINB>
+__global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   using F = Frag<E, D>;
   using LD = Lds<D, E>;
   constexpr bool BF = std::is_same<E, __bf16>::value;
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
   constexpr int PAIRS = kSubTile * CHUNKS;               // (row, chunk) slots of a sub-tile
   constexpr int PP = (PAIRS + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) char lds_kv[2][LD::TILE];
-  __shared__ f32x4 lds_A[NW][NBW][NM][64];               // [wave][block][row block][lane]
+  __shared__ f32x4 lds_A[AREG ? 1 : NW][AREG ? 1 : NBW][AREG ? 1 : NM][64];   // [wave][block][row block][lane]
   __shared__ int lds_pages[kPageCache];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -441,6 +441,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
   typename F::Q qf[NBW];
   RowState<D> st[NBW];
   float Mrow[NBW], Lrow[NBW];
+  f32x4 Areg[AREG ? NBW : 1][NM];
   int pos_c[NBW], blk_max[NBW];
   bool valid_c[NBW];
   int wave_min = 0x7fffffff, wave_max = -1;
@@ -482,7 +483,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
   // the wait before each LDS store counts exactly the later loads. Absent pages and sub-tiles
   // past the end read kNanRows (K) and kZeroRows (V), and so do V rows at or past seq_len:
   // no stale cache bytes reach an MFMA, and a row that needs an absent page comes out NaN.
-  constexpr int NPF = 4;
   u32x4 preK[NPF][PP], preV[NPF][PP];
   const int last = max(nsub - 1, 0);
   const char* nan_rows = (const char*)&kNanRows;
@@ -566,13 +566,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
         if (blk_max[cb] < j * S) continue;
         const bool act = pos_c[cb] >= j * S;
         float M = Mrow[cb], L = Lrow[cb], fa, fb;
-        fold_scalars(M, L, st[cb].m, st[cb].l, j == 0, fa, fb);
+        fold_scalars(M, L, st[cb].m, row_l(st[cb]), j == 0, fa, fb);
         if (act) {
           Mrow[cb] = M;
           Lrow[cb] = L;
 #pragma unroll
           for (int mb = 0; mb < NM; ++mb) {
-            f32x4& slot = lds_A[wave][cb][mb][lane];
+            f32x4& slot = AREG ? Areg[AREG ? cb : 0][mb] : lds_A[AREG ? 0 : wave][AREG ? 0 : cb][AREG ? 0 : mb][lane];
             f32x4 A = j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot;
 #pragma unroll
             for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb, j == 0);
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnParams a) {
     f32x4 R[NM];
 #pragma unroll
     for (int mb = 0; mb < NM; ++mb) {
-      const f32x4 A = lds_A[wave][cb][mb][lane];
+      const f32x4 A = AREG ? Areg[AREG ? cb : 0][mb] : lds_A[AREG ? 0 : wave][AREG ? 0 : cb][AREG ? 0 : mb][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) R[mb][e] = ok ? A[e] / Lrow[cb] : __builtin_nanf("");
     }
@@ -823,21 +823,24 @@ int dispatch_partials(const bi_attn_cfg* cfg, const AttnParams& a, hipStream_t s
   return bf ? launch_partials<__bf16, 64>(a, s) : launch_partials<float, 64>(a, s);
 }
 
-constexpr int kPrefillNBW = 2;
-
-template <typename E, int D, int NW>
+// bf16: two workgroups of 4 waves per CU (their barriers are independent, so one fills the
+// other's stalls), 2 column blocks per wave, A in registers, one staging set in flight (the
+// other workgroup's loads cover the latency). fp32: one workgroup of 4 waves, A in LDS.
+template <typename E, int D>
 int launch_prefill(const AttnParams& a, hipStream_t s) {
-  const int cols = NW * kPrefillNBW * 16;
-  const int tq = cols / a.group;
-  const dim3 grid((unsigned)((a.max_q_len + tq - 1) / tq), (unsigned)a.hkv, (unsigned)a.batch);
+  constexpr bool BF = std::is_same<E, __bf16>::value;
+  constexpr int NW = 4, NBW = 2, NPF = BF ? 1 : 4, MINB = BF ? 2 : 1;
+  constexpr bool AREG = BF;
   // sequences longer than the LDS page-id ring need the kernel that refills it
   const bool ring = (int64_t)a.max_seq_len + kSubTile > (int64_t)kPageCache * kPage;
+  const int tq = NW * NBW * 16 / a.group;
+  const dim3 grid((unsigned)((a.max_q_len + tq - 1) / tq), (unsigned)a.hkv, (unsigned)a.batch);
   if (a.group >= 16) {
-    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, false, true>), grid, dim3(64 * NW), 0, s, a);
-    else hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, false, false>), grid, dim3(64 * NW), 0, s, a);
+    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, true, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
+    else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, false, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
   } else {
-    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, true, true>), grid, dim3(64 * NW), 0, s, a);
-    else hipLaunchKernelGGL((prefill_kernel<E, D, kPrefillNBW, NW, true, false>), grid, dim3(64 * NW), 0, s, a);
+    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, true, true, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
+    else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, true, false, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
   }
   return launched();
 }
@@ -953,8 +956,8 @@ int bi_attn_prefill(const bi_attn_cfg* cfg, const void* q, const void* k_cache, 
   a.max_q_len = max_q_len;
   a.max_seq_len = max_seq_len;
   const bool bf = cfg->dtype == BI_BF16;
-  if (cfg->head_dim == 128) return bf ? launch_prefill<__bf16, 128, 8>(a, stream) : launch_prefill<float, 128, 4>(a, stream);
-  return bf ? launch_prefill<__bf16, 64, 8>(a, stream) : launch_prefill<float, 64, 4>(a, stream);
+  if (cfg->head_dim == 128) return bf ? launch_prefill<__bf16, 128>(a, stream) : launch_prefill<float, 128>(a, stream);
+  return bf ? launch_prefill<__bf16, 64>(a, stream) : launch_prefill<float, 64>(a, stream);
 }
 
 }  // extern "C"

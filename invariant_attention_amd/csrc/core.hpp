@@ -137,17 +137,19 @@ template <int D> struct Frag<__bf16, D> {
 #pragma unroll
     for (int s = 0; s < NKS; ++s) q.v[s] = zero_k();
   }
+  // Each score block s[b][kb] accumulates its k-steps in ascending order; the 2 NB chains are
+  // interleaved k-step by k-step so that consecutive MFMAs are independent.
   template <int NB, class KGet>
   __device__ static inline void qk(f32x4 (&s)[NB][2], KGet& getK, const Q (&q)[NB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int b = 0; b < NB; ++b) s[b][0] = s[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < NB; ++b) s[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < NKS; ++st) {
+      const u32x4 k0 = getK(0, st), k1 = getK(1, st);
 #pragma unroll
-      for (int st = 0; st < NKS; ++st) {
-        const u32x4 kf = getK(kb, st);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) s[b][kb] = mma_bf16(kf, q[b].v[st], s[b][kb]);
+      for (int b = 0; b < NB; ++b) {
+        s[b][0] = mma_bf16(k0, q[b].v[st], s[b][0]);
+        s[b][1] = mma_bf16(k1, q[b].v[st], s[b][1]);
       }
     }
   }
@@ -290,6 +292,8 @@ template <int D> struct Frag<float, D> {
 // by more than kLazy (so p <= 2^kLazy). The result is the same softmax; skipping most
 // rescales removes the acc *= alpha multiplies from most sub-tiles. The decision depends on
 // the row's own numbers only, so every route makes the same one.
+// l is kept per lane (the sum of the p values the lane holds); the row's l is the sum of its
+// four lanes' partials, taken once per split by row_l().
 constexpr float kLazy = 8.0f;
 
 template <int D> struct RowState {
@@ -297,6 +301,7 @@ template <int D> struct RowState {
   float m, l;
   f32x4 acc[NM];
 };
+template <int D> __device__ __forceinline__ float row_l(const RowState<D>& st) { return xor_sum(st.l); }
 
 __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballot_w64(v) != 0; }
 
@@ -322,39 +327,53 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
   float p[NB][2][4];
   float mnew[NB], lnew[NB], alpha[NB];
   bool need_any = false;
+  float x[NB][2][4], mxl[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float x[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[kb][r] = s[b][kb][r];
+      for (int r = 0; r < 4; ++r) x[b][kb][r] = s[b][kb][r];
     if (mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          x[kb][r] = (key0 + 16 * kb + 4 * g + r <= pos[b]) ? x[kb][r] : -__builtin_inff();
+          x[b][kb][r] = (key0 + 16 * kb + 4 * g + r <= pos[b]) ? x[b][kb][r] : -__builtin_inff();
     }
-    float mx = vmax(vmax3(x[0][0], x[0][1], x[0][2]),
-                    vmax3(x[0][3], x[1][0], vmax3(x[1][1], x[1][2], x[1][3])));
-    mx = xor_max(mx);
-    const float mt = mx * cscale;
+    mxl[b] = vmax(vmax3(x[b][0][0], x[b][0][1], x[b][0][2]),
+                  vmax3(x[b][0][3], x[b][1][0], vmax3(x[b][1][1], x[b][1][2], x[b][1][3])));
+  }
+  // A row raises its reference only if some lane of it holds a scaled score above m + kLazy
+  // (the scaled row max is the max of the lanes' scaled maxima: rounding is monotonic), so
+  // the row max butterfly runs only at a split start or when some lane of the wave needs it.
+  bool any_up = first;
+  if (!first) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) any_up = any_up || (mxl[b] * cscale > st[b].m + kLazy);
+  }
+  const bool full = first || wave_any(any_up);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
     bool need = false;
-    if (first) {
-      mnew[b] = mt;
+    if (full) {
+      const float mt = xor_max(mxl[b]) * cscale;
+      if (first) {
+        mnew[b] = mt;
+      } else {
+        need = mt > st[b].m + kLazy;
+        mnew[b] = need ? mt : st[b].m;
+      }
     } else {
-      need = mt > st[b].m + kLazy;
-      mnew[b] = need ? mt : st[b].m;
+      mnew[b] = st[b].m;
     }
     const float nm = -mnew[b];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[kb][r], cscale, nm));
-    float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
-               ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
-    rs = xor_sum(rs);
+      for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[b][kb][r], cscale, nm));
+    const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
+                     ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
     if (first) {
       lnew[b] = rs;
       alpha[b] = 0.f;
