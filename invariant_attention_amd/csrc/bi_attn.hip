@@ -487,19 +487,27 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   const int last = max(nsub - 1, 0);
   const char* nan_rows = (const char*)&kNanRows;
   const char* zero_rows = (const char*)kZeroRows;
+  // this thread's slots: row r of the sub-tile (key key0 + r, in page half r / kPage) and the
+  // byte offset of its 16-byte chunk inside a page
+  unsigned srow[PP], sin_page[PP];
+#pragma unroll
+  for (int k = 0; k < PP; ++k) {
+    const unsigned pair = (unsigned)min((int)threadIdx.x + k * NT, PAIRS - 1);
+    const unsigned r = pair / CHUNKS, ch = pair - r * CHUNKS;
+    srow[k] = r;
+    sin_page[k] = (r % kPage) * LD::ROWB + ch * 16;
+  }
   auto stage_load = [&](int u, u32x4 (&pk)[PP], u32x4 (&pv)[PP]) {
-    const int key0 = u * kSubTile;
 #pragma unroll
     for (int k = 0; k < PP; ++k) {
-      const int pair = min(threadIdx.x + k * NT, PAIRS - 1);
-      const int r = pair / CHUNKS, ch = pair - r * CHUNKS;
-      const int key = key0 + r;
-      const int lp = key / kPage;
+      const unsigned lp = 2u * (unsigned)u + srow[k] / kPage;
       const int page = u <= last ? lds_pages[lp % kPageCache] : -1;
-      const size_t in_page = (size_t)(key % kPage) * LD::ROWB + ch * 16;
-      const size_t off = (size_t)page * page_stride + in_page;
-      pk[k] = *(const u32x4*)(page >= 0 ? kbase + off : nan_rows + in_page);
-      pv[k] = *(const u32x4*)(page >= 0 && key < seq_len ? vbase + off : zero_rows + in_page);
+      const bool vin = u * kSubTile + (int)srow[k] < seq_len;
+      const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
+      const char* kp = page >= 0 ? kbase + off : nan_rows;
+      const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
+      pk[k] = *(const u32x4*)(kp + sin_page[k]);
+      pv[k] = *(const u32x4*)(vp + sin_page[k]);
     }
   };
   auto stage_store = [&](const u32x4 (&pk)[PP], const u32x4 (&pv)[PP]) {

@@ -335,11 +335,12 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[b][kb][r] = s[b][kb][r];
     if (mask) {
+      // key key0 + 16 kb + 4 g + r is visible to the row iff 16 kb + r <= pos - key0 - 4 g
+      const int lim = pos[b] - key0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[b][kb][r] = (key0 + 16 * kb + 4 * g + r <= pos[b]) ? x[b][kb][r] : -__builtin_inff();
+        for (int r = 0; r < 4; ++r) x[b][kb][r] = (16 * kb + r <= lim) ? x[b][kb][r] : -__builtin_inff();
     }
     mxl[b] = vmax(vmax3(x[b][0][0], x[b][0][1], x[b][0][2]),
                   vmax3(x[b][0][3], x[b][1][0], vmax3(x[b][1][1], x[b][1][2], x[b][1][3])));
