@@ -184,16 +184,18 @@ def run_decode_bench(args, result):
     comb = np.mean([t.ms(2, 3) for t in timers])
 
     # variant timing (same step shape)
-    for i in range(args.warmup):
-        step(i, cfg_v, ws_v)
-    whole_v = Timer(2)
-    torch.cuda.synchronize()
-    whole_v.mark(0)
-    for i in range(args.steps):
-        step(i, cfg_v, ws_v)
-    whole_v.mark(1)
-    torch.cuda.synchronize()
-    var_step = whole_v.ms(0, 1) / args.steps
+    var_step = None
+    if not args.profile_run:
+        for i in range(args.warmup):
+            step(i, cfg_v, ws_v)
+        whole_v = Timer(2)
+        torch.cuda.synchronize()
+        whole_v.mark(0)
+        for i in range(args.steps):
+            step(i, cfg_v, ws_v)
+        whole_v.mark(1)
+        torch.cuda.synchronize()
+        var_step = whole_v.ms(0, 1) / args.steps
 
     nb = decode_bytes(shape, bt.seq_lens)
     step_ms = max(wall * 1e3, gpu_step)
@@ -212,12 +214,12 @@ def run_decode_bench(args, result):
                           "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": part}
     result["decode_breakdown_ms"] = {"page_update": pu, "partials": part, "combine": comb,
                                      "step_events": gpu_step, "step_wall": wall * 1e3}
-    result["variant_slowdown"] = {"decode": gpu_step / var_step - 1.0,
+    result["variant_slowdown"] = {"decode": gpu_step / var_step - 1.0 if var_step else None,
                                   "decode_ms": {"invariant": gpu_step, "split_by_batch": var_step}}
 
     # --- sweep over batch sizes (first B sequences of the same workload)
     sweep = []
-    for Bs in (1, 2, 4, 8, 16, 32, 64):
+    for Bs in (() if args.profile_run else (1, 2, 4, 8, 16, 32, 64)):
         idx = torch.arange(Bs, device="cuda")
         qb, ptb, slb = q[idx].contiguous(), pt[idx].contiguous(), sl[idx].contiguous()
         ob = torch.empty((Bs, shape.num_q_heads, shape.head_dim), device="cuda")
@@ -294,7 +296,7 @@ def run_prefill_bench(args, result):
 
     n = max(3, args.steps // 5)
     kern, step_ms, wall = run(cfg, n, max(1, args.warmup // 5))
-    kern_v, step_v, _ = run(cfg_of(shape, bi.BI_SPLIT_BY_BATCH), n, 1)
+    kern_v = None if args.profile_run else run(cfg_of(shape, bi.BI_SPLIT_BY_BATCH), n, 1)[0]
     fl = prefill_flops(bt)
     tf = fl / (kern * 1e-3) / 1e12
     result["prefill"] = {
@@ -309,7 +311,7 @@ def run_prefill_bench(args, result):
                                   "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": tf / BF16_PEAK_TFLOPS,
                                   "traffic": profiled_traffic("prefill_kernel")}
-    result["variant_slowdown"]["prefill"] = kern / kern_v - 1.0
+    result["variant_slowdown"]["prefill"] = kern / kern_v - 1.0 if kern_v else None
     result["variant_slowdown"]["prefill_ms"] = {"invariant": kern, "split_by_batch": kern_v}
     return bt, ref
 
@@ -362,6 +364,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="measure the prefill workload alone (no headline value)")
     ap.add_argument("--cpu-samples", type=int, default=64)
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only the headline decode steps and the prefill workload (no split-by-batch "
+                         "variant, no batch sweep), so a profiler sees one workload per kernel")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
