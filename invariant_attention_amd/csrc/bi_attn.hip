@@ -93,8 +93,9 @@ __device__ __forceinline__ const char* kv_row(const char* cache, const AttnParam
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode. The work items of a KV head are the splits (b, j) of every sequence, in ascending b
-// and then j. The grid holds as many waves as the device keeps resident; of W waves per head,
+// Decode. The work items of a KV head are the splits (b, j) of every sequence (every split but
+// the last first, then the last splits). The grid holds as many waves as the device keeps
+// resident; of W waves per head,
 // wave w takes items w, w + W, w + 2W, ..., so every resident wave (and so every CU) gets the
 // same share of the work, within one item, and no workgroup exits at once. Per item, operands
 // stream from HBM straight into MFMA registers with two sub-tiles in flight: the loads of
@@ -137,32 +138,53 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   auto splits_of = [&](int len) {
     return (len > 0 && len <= a.max_seq_len) ? (len - 1) / split_len(a, len) + 1 : 0;
   };
-  int total = 0;
-  for (int cb = 0; cb < a.batch; cb += 64) total += wave_sum_i(splits_of(chunk_len(cb)));
-  total = __builtin_amdgcn_readfirstlane(total);
+  // Items in two runs: first every split but the last of each sequence (b, then j), then the
+  // last split of each sequence (b). A last split is the only one that can be short, so the
+  // items handed out last (to the waves that get one more) are the cheap ones.
+  int total_full = 0, total_last = 0;
+  for (int cb = 0; cb < a.batch; cb += 64) {
+    const int nj = splits_of(chunk_len(cb));
+    total_full += wave_sum_i(max(nj - 1, 0));
+    total_last += wave_sum_i(nj > 0 ? 1 : 0);
+  }
+  total_full = __builtin_amdgcn_readfirstlane(total_full);
+  const int total = total_full + __builtin_amdgcn_readfirstlane(total_last);
   if (w >= total) return;
-  // Item i -> (sequence, split), for increasing i: a cursor over the chunks of 64 sequences
-  // (inclusive prefix sums of their split counts in incl_v; `before` items precede the chunk).
-  int cb = 0, before = 0;
-  int len_v = chunk_len(0);
-  int nj_v = splits_of(len_v);
-  int incl_v = wave_incl_scan(nj_v, lane);
-  auto locate = [&](int i, int& ob, int& oj) {
+  // Item i -> (sequence, split, length) for increasing i: one cursor per run over the chunks
+  // of 64 sequences (inclusive prefix sums of the run's per-sequence item counts in incl;
+  // `before` items of the run precede the chunk).
+  auto count_of = [&](int run, int len) {
+    const int nj = splits_of(len);
+    return run == 0 ? max(nj - 1, 0) : (nj > 0 ? 1 : 0);
+  };
+  int cb0 = 0, before0 = 0, incl0 = wave_incl_scan(count_of(0, chunk_len(0)), lane);
+  int cb1 = 0, before1 = 0, incl1 = wave_incl_scan(count_of(1, chunk_len(0)), lane);
+  auto seek = [&](int run, int k, int& cb, int& before, int& incl) {
     for (;;) {
-      const int tot = __builtin_amdgcn_readlane(incl_v, 63);
-      if (before + tot > i) break;
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (before + tot > k) break;
       before += tot;
       cb += 64;
-      len_v = chunk_len(cb);
-      nj_v = splits_of(len_v);
-      incl_v = wave_incl_scan(nj_v, lane);
+      incl = wave_incl_scan(count_of(run, chunk_len(cb)), lane);
     }
-    const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before + incl_v <= i));
-    ob = cb + nb;
-    oj = i - before - (nb > 0 ? __builtin_amdgcn_readlane(incl_v, nb - 1) : 0);
+    const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before + incl <= k));
+    return nb;
   };
-  int item = w, b = 0, j = 0;
-  locate(item, b, j);
+  auto locate = [&](int i, int& ob, int& oj, int& olen) {
+    if (i < total_full) {
+      const int nb = seek(0, i, cb0, before0, incl0);
+      ob = cb0 + nb;
+      oj = i - before0 - (nb > 0 ? __builtin_amdgcn_readlane(incl0, nb - 1) : 0);
+      olen = a.seq_lens[ob];   // uniform: a scalar load, which leaves the vector loads in flight
+    } else {
+      const int nb = seek(1, i - total_full, cb1, before1, incl1);
+      ob = cb1 + nb;
+      olen = a.seq_lens[ob];
+      oj = splits_of(olen) - 1;
+    }
+  };
+  int item = w, b = 0, j = 0, len0 = 0;
+  locate(item, b, j, len0);
 
   const size_t head_stride = (size_t)kPage * ROWB;
   const size_t page_stride = (size_t)a.hkv * head_stride;
@@ -200,9 +222,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
     }
     if (item + W >= total) return false;
     item += W;
-    int nb2, nj2;
-    locate(item, nb2, nj2);
-    un = make_unit(nb2, nj2, 0, __builtin_amdgcn_readlane(len_v, nb2 - cb));
+    int nb2, nj2, len2;
+    locate(item, nb2, nj2, len2);
+    un = make_unit(nb2, nj2, 0, len2);
     return true;
   };
   auto unit_pages = [&](const Unit& u) {
@@ -227,7 +249,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   // this wave touches its slice, and one wave's LDS accesses complete in order)
   __shared__ __attribute__((aligned(16))) float lds_part_all[kWaves][NB * 16 * D];
   float* lds_part = lds_part_all[threadIdx.x >> 6];
-  Unit u = make_unit(b, j, 0, __builtin_amdgcn_readlane(len_v, b - cb)), un;
+  Unit u = make_unit(b, j, 0, len0), un;
   int pg = unit_pages(u), pgn = -1;
   typename F::Q qf[NB];
   load_q_of(qf, u.b, true);
