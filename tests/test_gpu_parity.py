@@ -154,3 +154,31 @@ def test_bad_page_entry_gives_nan_rows_only_where_needed(bad):
     got_d = run_decode(cfg, dd)
     assert torch.isnan(got_d[1]).all()
     assert_bitwise(got_d[[0, 2]], clean_d[[0, 2]], f"decode rows of other sequences ({bad})")
+
+
+def test_decode_many_sequences_with_invalid_lengths():
+    """150 sequences (the work split walks several chunks of 64 sequences); rows whose length is
+    0 or above max_seq_len come out NaN, and every other row keeps its bits and its parity."""
+    shape = AttnShape(32, 4, 128, 16, 256, "bf16")
+    cfg = cfg_for(shape)
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(1, 1500, 150)]
+    seqs = [SeqSpec(i, L - 1, 1) for i, L in enumerate(lens)]
+    bt = build_batch(shape, seqs, seed=42, page_seed=43, extra_pages=8)
+    d = to_device(bt, cfg)
+    _print_case("decode 150 sequences")
+    clean = run_decode(cfg, d)
+    bad = [3, 64, 70, 128, 149]
+    sl = d.seq_lens.clone()
+    for i, r in enumerate(bad):
+        sl[r] = 0 if i % 2 == 0 else bt.max_seq_len + 5
+    out = torch.full_like(clean, float("nan"))
+    ws = torch.empty(bi.bi_attn_workspace_bytes(cfg, 150, bt.max_seq_len) // 4 + 64, device="cuda")
+    bi.bi_attn_decode(cfg, d.q, d.k_cache, d.v_cache, d.page_table, sl, bt.max_seq_len, out, ws)
+    assert torch.isnan(out[bad]).all()
+    good = [r for r in range(150) if r not in bad]
+    assert_bitwise(out[good], clean[good], "valid rows next to invalid ones")
+    rows = [(r, h) for r in good[::7] for h in (0, 13, 31)]
+    ref = oracle_rows(bt, rows)
+    got = np.stack([clean[r, h].cpu().numpy() for r, h in rows])
+    assert_parity(got, ref, "decode 150 sequences, sampled rows")
