@@ -425,6 +425,76 @@ template <int D, typename E> struct Lds {
 };
 constexpr int kPageCache = 2048;
 
+// Longest-first order of the prefill work. A work item is (sequence b, query tile t); its cost
+// is its sub-tile count n(b, t) = (first_pos + min((t + 1) tq, n_new) + 31) / 32, which never
+// decreases with t. Workgroup rank i takes the i-th item in the order (n descending, then b
+// ascending, then t ascending), so the longest tiles start first and the short ones fill the
+// end of the grid. Which workgroup computes an item never changes its numbers.
+struct PfSeq {
+  int fp, n, nt;   // first position, new tokens, tiles (0: the sequence has no items)
+  bool bad;        // invalid lengths: its tiles cost nothing (they only write NaN rows)
+};
+__device__ __forceinline__ PfSeq pf_seq(const AttnParams& a, int b, int tq) {
+  PfSeq s{0, 0, 0, false};
+  if (b >= a.batch) return s;
+  const int q0 = a.q_starts[b], q1 = a.q_starts[b + 1];
+  if (q1 > a.total_tokens || q0 < 0 || q1 <= q0) return s;
+  const int len = a.seq_lens[b];
+  s.n = q1 - q0;
+  s.nt = (s.n + tq - 1) / tq;
+  s.bad = len > a.max_seq_len || s.n > len;
+  s.fp = len - s.n;
+  return s;
+}
+// tiles of the sequence whose sub-tile count exceeds K (K >= -1): n(b, t) > K exactly when
+// min((t + 1) tq, n_new) >= 32 K + 1 - first_pos
+// (tq = 2^lg: the group size divides 128)
+__device__ __forceinline__ int pf_tiles_above(const PfSeq& s, int K, int lg) {
+  if (s.nt <= 0) return 0;
+  if (s.bad) return K < 0 ? s.nt : 0;
+  const int R = 32 * K + 1 - s.fp;
+  if (R > s.n) return 0;
+  return s.nt - (R <= 0 ? 0 : ((R + (1 << lg) - 1) >> lg) - 1);
+}
+// Item of rank i for this wave (wave-uniform); false when i is past the last item.
+__device__ bool pf_item(const AttnParams& a, int tq, int i, int& ob, int& otile) {
+  const int lane = threadIdx.x & 63;
+  const int lg = __builtin_ctz(tq);
+  const int chunks = (a.batch + 63) / 64;
+  const PfSeq s0 = pf_seq(a, lane, tq);   // the first 64 sequences stay in registers
+  auto seq_of = [&](int ch) { return ch == 0 ? s0 : pf_seq(a, 64 * ch + lane, tq); };
+  auto count_above = [&](int K) {
+    int c = 0;
+    for (int ch = 0; ch < chunks; ++ch) c += wave_sum_i(pf_tiles_above(seq_of(ch), K, lg));
+    return __builtin_amdgcn_readfirstlane(c);
+  };
+  if (i >= count_above(-1)) return false;
+  // smallest K with count_above(K) <= i: the cost of item i
+  int lo = -1, hi = (a.max_seq_len + 31) / 32;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (count_above(mid) <= i) hi = mid;
+    else lo = mid;
+  }
+  int r = i - count_above(hi);   // rank among the items of cost hi, in (b, t) order
+  for (int ch = 0; ch < chunks; ++ch) {
+    const PfSeq s = seq_of(ch);
+    const int ge = pf_tiles_above(s, hi - 1, lg), gt = pf_tiles_above(s, hi, lg);
+    const int e = ge - gt;   // tiles t in [nt - ge, nt - gt) cost exactly hi
+    const int incl = wave_incl_scan(e, lane);
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(incl > r);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const int before = __shfl(incl - e, l);
+      ob = __builtin_amdgcn_readfirstlane(64 * ch + l);
+      otile = __builtin_amdgcn_readfirstlane(__shfl(s.nt - ge, l) + (r - before));
+      return true;
+    }
+    r -= __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  }
+  return false;
+}
+
 template <typename E, int D, int NBW, int NW, bool LANESEL, bool RING, int NPF, bool AREG, int MINB>
 __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   using F = Frag<E, D>;
@@ -442,14 +512,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int b = blockIdx.z, kvh = blockIdx.y;
   const int G = a.group;
   const int tq = COLS / G;                       // tokens per tile (G divides COLS)
+  // workgroup = (item rank, KV head); items longest first
+  const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
+  int b = 0, tile = 0;
+  if (!pf_item(a, tq, (int)(blockIdx.x / (unsigned)a.hkv), b, tile)) return;
   const int q0 = a.q_starts[b], q1 = a.q_starts[b + 1];
   const int n_new = q1 - q0;
-  const int n_tiles = (n_new + tq - 1) / tq;
-  const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;   // later (longer) tiles first
-  if (tile >= n_tiles || q1 > a.total_tokens || q0 < 0) return;
   const int t0 = tile * tq;
   const int seq_len = a.seq_lens[b];
   const bool bad_seq = seq_len > a.max_seq_len || n_new > seq_len;
@@ -864,7 +934,10 @@ int launch_prefill(const AttnParams& a, hipStream_t s) {
   // sequences longer than the LDS page-id ring need the kernel that refills it
   const bool ring = (int64_t)a.max_seq_len + kSubTile > (int64_t)kPageCache * kPage;
   const int tq = NW * NBW * 16 / a.group;
-  const dim3 grid((unsigned)((a.max_q_len + tq - 1) / tq), (unsigned)a.hkv, (unsigned)a.batch);
+  // one workgroup per (tile, KV head); workgroups past the real item count exit at once
+  const int64_t wgs = (int64_t)((a.max_q_len + tq - 1) / tq) * a.batch * a.hkv;
+  if (wgs > 0x7fffffff) return BI_EUNSUPPORTED;
+  const dim3 grid((unsigned)wgs);
   if (a.group >= 16) {
     if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, true, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
     else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, false, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);

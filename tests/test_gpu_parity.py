@@ -182,3 +182,37 @@ def test_decode_many_sequences_with_invalid_lengths():
     ref = oracle_rows(bt, rows)
     got = np.stack([clean[r, h].cpu().numpy() for r, h in rows])
     assert_parity(got, ref, "decode 150 sequences, sampled rows")
+
+
+@pytest.mark.parametrize("hq", [64, 32])
+def test_prefill_many_sequences_with_invalid_lengths(hq):
+    """90 sequences of mixed prefix and chunk lengths (some chunks empty): the longest-first
+    order of the query tiles walks several chunks of 64 sequences and many equal costs. Every
+    token of a valid sequence gets a finite row within parity; making some lengths invalid
+    turns exactly their tokens NaN and leaves every other row's bits as they were."""
+    shape = AttnShape(hq, 4, 128, 16, 256, "bf16")
+    cfg = cfg_for(shape)
+    rng = np.random.default_rng(51)
+    seqs = [SeqSpec(i, int(rng.integers(0, 600)), int(rng.integers(0, 40))) for i in range(90)]
+    bt = build_batch(shape, seqs, seed=52, page_seed=53, extra_pages=8)
+    d = to_device(bt, cfg)
+    _print_case("prefill 90 sequences", hq)
+    clean = run_prefill(cfg, d)
+    assert torch.isfinite(clean).all(), "a query tile was skipped"
+    qs = bt.q_starts
+    bad = [b for b in (2, 33, 64, 65, 89) if qs[b + 1] > qs[b]]
+    sl = d.seq_lens.clone()
+    for i, b in enumerate(bad):
+        sl[b] = (qs[b + 1] - qs[b]) - 1 if i % 2 == 0 else bt.max_seq_len + 5
+    out = torch.full_like(clean, float("nan"))
+    bi.bi_attn_prefill(cfg, d.q, d.k_cache, d.v_cache, d.page_table, d.q_starts, sl,
+                       d.max_q_len, d.max_seq_len, out)
+    bad_rows = np.concatenate([np.arange(qs[b], qs[b + 1]) for b in bad])
+    good_rows = np.setdiff1d(np.arange(bt.total_tokens), bad_rows)
+    assert torch.isnan(out[torch.from_numpy(bad_rows)]).all()
+    assert_bitwise(out[torch.from_numpy(good_rows)], clean[torch.from_numpy(good_rows)],
+                   "valid rows next to invalid sequences")
+    rows = [(int(r), h) for r in good_rows[::11] for h in (0, hq // 2 + 1, hq - 1)]
+    ref = oracle_rows(bt, rows)
+    got = np.stack([clean[r, h].cpu().numpy() for r, h in rows])
+    assert_parity(got, ref, "prefill 90 sequences, sampled rows")
