@@ -646,7 +646,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
       };
       if (key0 <= wave_min) {
         // every valid row of the wave reaches key0: all blocks advance together
-        subtile_step<E, D, NBW, false>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
+        subtile_step<E, D, NBW, false, BF>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
                                        key0 + kSubTile - 1 > wave_min);
       } else {
         // some row stops before key0 (the diagonal of the tile): block by block, and row by
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
 #pragma unroll
         for (int cb = 0; cb < NBW; ++cb)
           if (blk_max[cb] >= key0)
-            subtile_step<E, D, 1, LANESEL>(&st[cb], &qf[cb], &pos_c[cb], getK, getV, a.cscale,
+            subtile_step<E, D, 1, LANESEL, BF>(&st[cb], &qf[cb], &pos_c[cb], getK, getV, a.cscale,
                                            key0, g, first, true);
       }
     }

@@ -138,27 +138,37 @@ template <int D> struct Frag<__bf16, D> {
     for (int s = 0; s < NKS; ++s) q.v[s] = zero_k();
   }
   // Each score block s[b][kb] accumulates its k-steps in ascending order; the 2 NB chains are
-  // interleaved k-step by k-step so that consecutive MFMAs are independent.
-  template <int NB, class KGet>
+  // interleaved k-step by k-step so that consecutive MFMAs are independent. PIPE (operands
+  // read from LDS): the reads of k-step st + 1 are issued before the MFMAs of k-step st.
+  template <int NB, bool PIPE = false, class KGet>
   __device__ static inline void qk(f32x4 (&s)[NB][2], KGet& getK, const Q (&q)[NB]) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) s[b][0] = s[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 k0 = getK(0, 0), k1 = getK(1, 0);
 #pragma unroll
     for (int st = 0; st < NKS; ++st) {
-      const u32x4 k0 = getK(0, st), k1 = getK(1, st);
+      u32x4 n0 = k0, n1 = k1;
+      if (st + 1 < NKS) {
+        n0 = getK(0, st + 1);
+        n1 = getK(1, st + 1);
+      }
+      if (PIPE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         s[b][0] = mma_bf16(k0, q[b].v[st], s[b][0]);
         s[b][1] = mma_bf16(k1, q[b].v[st], s[b][1]);
       }
+      k0 = n0;
+      k1 = n1;
     }
   }
   // acc += P V with P = P_hi + P_lo, both bf16 (round to nearest even), hi first.
   // getV(mb) returns the A operand of row block mb: 8 bf16 of one head-dim row d for the key
   // slots vkey(0..7, g). Which d a (row block, lane) holds is the caller's choice; each
   // output element's dot product is the same whichever MFMA row computes it.
-  template <int NB, class VGet>
+  template <int NB, bool PIPE = false, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
+    u32x4 vf = getV(0), vf1 = getV(1);   // (PIPE: in flight during the conversions)
     u32x4 H[NB], L[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -174,12 +184,16 @@ template <int D> struct Frag<__bf16, D> {
     }
 #pragma unroll
     for (int mb = 0; mb < NM; ++mb) {
-      const u32x4 vf = getV(mb);
+      // PIPE: the reads of row block mb + 2 are issued before the MFMAs of row block mb
+      const u32x4 vn = mb + 2 < NM ? getV(mb + 2) : vf;
+      if (PIPE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         acc[b][mb] = mma_bf16(vf, H[b], acc[b][mb]);
         acc[b][mb] = mma_bf16(vf, L[b], acc[b][mb]);
       }
+      vf = vf1;
+      vf1 = vn;
     }
   }
   // A operand of row block mb from raw V chunks in registers (row d = NM c + mb): slot pair
@@ -257,7 +271,7 @@ template <int D> struct Frag<float, D> {
 #pragma unroll
     for (int s = 0; s < NKS; ++s) q.v[s] = 0.f;
   }
-  template <int NB, class KGet>
+  template <int NB, bool PIPE = false, class KGet>
   __device__ static inline void qk(f32x4 (&s)[NB][2], KGet& getK, const Q (&q)[NB]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -272,7 +286,7 @@ template <int D> struct Frag<float, D> {
     }
   }
   // getV(i) returns the lane's raw V chunk (NM floats, dims NM c .. NM c + NM) of key slot i.
-  template <int NB, class VGet>
+  template <int NB, bool PIPE = false, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -312,7 +326,9 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 //   first: first sub-tile of the split (state reset, not rescaled)
 //   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
 //   SEL:   rows with pos < key0 keep their state (only when a block mixes such rows)
-template <typename E, int D, int NB, bool SEL, class KGet, class VGet>
+//   PIPE:  operand reads are issued ahead of the MFMAs that use them (LDS operands): K one
+//          k-step ahead, V two row blocks ahead
+template <typename E, int D, int NB, bool SEL, bool PIPE = false, class KGet, class VGet>
 __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Frag<E, D>::Q* q,
                                              const int* pos, KGet&& getK, VGet&& getV,
                                              float cscale, int key0, int g, bool first,
@@ -323,7 +339,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 #pragma unroll
   for (int b = 0; b < NB; ++b) qv[b] = q[b];
   f32x4 s[NB][2];
-  F::template qk<NB>(s, getK, qv);
+  F::template qk<NB, PIPE>(s, getK, qv);
   float p[NB][2][4];
   float mnew[NB], lnew[NB], alpha[NB];
   bool need_any = false;
@@ -392,7 +408,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb)
         acc[b][mb] = first ? f32x4{0.f, 0.f, 0.f, 0.f} : st[b].acc[mb] * alpha[b];
-    F::template pv<NB>(acc, getV, p);
+    F::template pv<NB, PIPE>(acc, getV, p);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (pos[b] >= key0) {
@@ -420,7 +436,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb) accl[b][mb] = st[b].acc[mb];
-    F::template pv<NB>(accl, getV, p);
+    F::template pv<NB, PIPE>(accl, getV, p);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       st[b].m = mnew[b];
