@@ -589,11 +589,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     srow[k] = r;
     sin_page[k] = (r % kPage) * LD::ROWB + ch * 16;
   }
+  // When the rows of each slot lie in one page (a page's row chunks are a multiple of the
+  // thread count), the page id and the K address are wave-uniform (scalar registers).
+  constexpr bool UNI = (kPage * CHUNKS) % NT == 0;
   auto stage_load = [&](int u, u32x4 (&pk)[PP], u32x4 (&pv)[PP]) {
 #pragma unroll
     for (int k = 0; k < PP; ++k) {
-      const unsigned lp = 2u * (unsigned)u + srow[k] / kPage;
-      const int page = u <= last ? lds_pages[lp % kPageCache] : -1;
+      const unsigned half = UNI ? (unsigned)(k * NT / (kPage * CHUNKS)) : srow[k] / kPage;
+      const unsigned lp = 2u * (unsigned)u + half;
+      int page = u <= last ? lds_pages[lp % kPageCache] : -1;
+      if (UNI) page = __builtin_amdgcn_readfirstlane(page);
       const bool vin = u * kSubTile + (int)srow[k] < seq_len;
       const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
       const char* kp = page >= 0 ? kbase + off : nan_rows;

@@ -373,6 +373,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     bool need = false;
+    alpha[b] = first ? 0.f : 1.0f;
     if (full) {
       const float mt = xor_max(mxl[b]) * cscale;
       if (first) {
@@ -380,6 +381,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
       } else {
         need = mt > st[b].m + kLazy;
         mnew[b] = need ? mt : st[b].m;
+        if (need) alpha[b] = ex2(st[b].m - mnew[b]);
       }
     } else {
       mnew[b] = st[b].m;
@@ -391,13 +393,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
       for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[b][kb][r], cscale, nm));
     const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
                      ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
-    if (first) {
-      lnew[b] = rs;
-      alpha[b] = 0.f;
-    } else {
-      alpha[b] = need ? ex2(st[b].m - mnew[b]) : 1.0f;
-      lnew[b] = __builtin_fmaf(st[b].l, alpha[b], rs);
-    }
+    lnew[b] = first ? rs : __builtin_fmaf(st[b].l, alpha[b], rs);
     if (SEL && pos[b] < key0) need = false;
     need_any = need_any || need;
   }
