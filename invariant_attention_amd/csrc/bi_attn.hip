@@ -346,66 +346,101 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
 }
 
 // Combine. The partials of one (sequence, KV head) and split are a contiguous [group][D] block;
-// a wave owns 256 consecutive floats of that block (lane: 4 floats of one row), folds them over
-// the splits in ascending j and writes A / L. Loads of kCombU splits are issued together, the
-// first ones before the row's split count is known.
-constexpr int kCombU = 16;
-template <int D>
+// a wave owns 64 FPL consecutive floats of that block (lane: FPL floats of one row), folds them
+// over the splits in ascending j and writes A / L. The accumulator loads run U splits ahead of
+// the fold in a ring of U register slots (slot u holds split j with j % U == u; a slot is
+// refilled as soon as it is folded), the first U before the row's split count is known. Loads
+// past the last split re-read it and are not folded, so every step issues the same loads.
+// With one float per lane a wave covers part of one row, and the (m, l) pairs of 64 splits
+// come in one load (lane i: split j0 + i), read out with readlane; with four floats per lane
+// every split's pairs are loaded with its accumulators.
+template <int FPL> struct CombVec;
+template <> struct CombVec<1> { typedef float T; };
+template <> struct CombVec<4> { typedef f32x4 T; };
+template <int D, int FPL, int U>
 __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
+  using V = typename CombVec<FPL>::T;
+  constexpr bool WIN = FPL == 1;   // (m, l) in 64-split windows (one window per ring turn)
+  static_assert(!WIN || U == 64, "one (m, l) window per ring turn");
   const int lane = threadIdx.x & 63;
   const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
   const int G = a.group;
-  const int chunks = (G * D + 255) / 256;              // waves per (sequence, KV head)
-  const int rg = gw / chunks, q = gw - rg * chunks;   // rg = b Hkv + kvh
+  const int chunks = (G * D + 64 * FPL - 1) / (64 * FPL);   // waves per (sequence, KV head)
+  const int rg = gw / chunks, q = gw - rg * chunks;         // rg = b Hkv + kvh
   if (rg >= a.batch * a.hkv) return;
   const int b = rg / a.hkv;
-  const int f = 256 * q + 4 * lane;                   // float of the [G][D] block
+  const int f = 64 * FPL * q + FPL * lane;                  // float of the [G][D] block
   if (f >= G * D) return;
   const int hl = f / D, d0 = f - hl * D;
-  float* o = a.out + ((size_t)rg * G + hl) * D + d0;   // row b Hq + kvh G + hl
-  const size_t blk0 = (size_t)rg * a.jmax * G;        // split 0 of the row group
+  float* o = a.out + ((size_t)rg * G + hl) * D + d0;         // row b Hq + kvh G + hl
+  const size_t blk0 = (size_t)rg * a.jmax * G;              // split 0 of the row group
   const float2* ml = a.ws_ml + blk0 + hl;
   const float* acc = a.ws_acc + blk0 * D + f;
   const size_t ml_step = G, acc_step = (size_t)G * D;
-  // the first kCombU splits' loads go out with the length's (the workspace holds jmax splits;
-  // those past the row's own count are read but not folded)
   const int seq_len = a.seq_lens[b];
-  float2 mlj[kCombU];
-  f32x4 accj[kCombU];
+  float2 mlj[WIN ? 1 : U], mlw = {0.f, 0.f}, mlw_next = {0.f, 0.f};
+  V accj[U];
+  if (WIN) {
+    mlw = ml[min(lane, a.jmax - 1) * ml_step];
+    mlw_next = ml[min(64 + lane, a.jmax - 1) * ml_step];
+  }
 #pragma unroll
-  for (int u = 0; u < kCombU; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int jj = min(u, a.jmax - 1);
-    mlj[u] = ml[jj * ml_step];
-    accj[u] = *(const f32x4*)(acc + jj * acc_step);
+    if (!WIN) mlj[u] = ml[jj * ml_step];
+    accj[u] = *(const V*)(acc + jj * acc_step);
   }
   if (seq_len <= 0 || seq_len > a.max_seq_len) {
-    *(f32x4*)o = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+#pragma unroll
+    for (int e = 0; e < FPL; ++e) o[e] = __builtin_nanf("");
     return;
   }
   const int J = (seq_len - 1) / split_len(a, seq_len) + 1;
   float M = 0.f, L = 0.f;
-  f32x4 A = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < J; j0 += kCombU) {
-    if (j0 > 0) {
+  float A[FPL];
 #pragma unroll
-      for (int u = 0; u < kCombU; ++u) {
-        const int jj = min(j0 + u, J - 1);            // in range; the extra ones are not folded
-        mlj[u] = ml[jj * ml_step];
-        accj[u] = *(const f32x4*)(acc + jj * acc_step);
-      }
+  for (int e = 0; e < FPL; ++e) A[e] = 0.f;
+  for (int j0 = 0; j0 < J; j0 += U) {
+    float2 mw = mlw;
+    if (WIN && j0 > 0) {
+      mw = mlw_next;
+      mlw_next = ml[min(j0 + 64 + lane, J - 1) * ml_step];
     }
 #pragma unroll
-    for (int u = 0; u < kCombU; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (j0 + u < J) {
         const bool first = (j0 + u) == 0;
+        float m, l;
+        if (WIN) {
+          m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mw.x), u));
+          l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mw.y), u));
+        } else {
+          m = mlj[WIN ? 0 : u].x;
+          l = mlj[WIN ? 0 : u].y;
+        }
         float fa, fb;
-        fold_scalars(M, L, mlj[u].x, mlj[u].y, first, fa, fb);
+        fold_scalars(M, L, m, l, first, fa, fb);
+        const V x = accj[u];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], accj[u][e], fa, fb, first);
+        for (int e = 0; e < FPL; ++e) {
+          float xe;
+          if constexpr (FPL == 1) xe = x;
+          else xe = x[e];
+          A[e] = fold_elem(A[e], xe, fa, fb, first);
+        }
       }
+      const int jn = min(j0 + u + U, J - 1);
+      if (!WIN) mlj[u] = ml[jn * ml_step];
+      accj[u] = *(const V*)(acc + jn * acc_step);
     }
   }
-  *(f32x4*)o = f32x4{A[0] / L, A[1] / L, A[2] / L, A[3] / L};
+  V r;
+  if constexpr (FPL == 1) r = A[0] / L;
+  else {
+#pragma unroll
+    for (int e = 0; e < FPL; ++e) r[e] = A[e] / L;
+  }
+  *(V*)o = r;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -878,11 +913,23 @@ int launch_partials(const AttnParams& a, hipStream_t s) {
   return launch_partials_nb<E, D, 4>(a, s);
 }
 
-int launch_combine(const AttnParams& a, int D, hipStream_t s) {
-  const int64_t waves = (int64_t)a.batch * a.hkv * ((a.group * D + 255) / 256);
+// Lane width of the combine: up to 32 splits per row, four floats per lane and every split's
+// loads issued at once; beyond, one float per lane (four times the waves) and a 64-split ring,
+// so that a few long sequences still keep enough loads in flight.
+template <int D, int FPL, int U>
+void launch_combine_w(const AttnParams& a, hipStream_t s) {
+  const int64_t waves = (int64_t)a.batch * a.hkv * ((a.group * D + 64 * FPL - 1) / (64 * FPL));
   const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
-  if (D == 128) hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((combine_kernel<D, FPL, U>), grid, dim3(kThreads), 0, s, a);
+}
+template <int D>
+void launch_combine_d(const AttnParams& a, hipStream_t s) {
+  if (a.jmax <= 32) launch_combine_w<D, 4, 32>(a, s);
+  else launch_combine_w<D, 1, 64>(a, s);
+}
+int launch_combine(const AttnParams& a, int D, hipStream_t s) {
+  if (D == 128) launch_combine_d<128>(a, s);
+  else launch_combine_d<64>(a, s);
   return launched();
 }
 
