@@ -162,38 +162,71 @@ template <int D> struct Frag<__bf16, D> {
       k1 = n1;
     }
   }
-  // acc += P V with P = P_hi + P_lo, both bf16 (round to nearest even), hi first.
+  // acc += P_hi V and acc += P_lo V: P_hi = bf16(p), P_lo = bf16(p - P_hi) (round to nearest
+  // even), P_lo zero in the lanes without lo_row, whose accumulators then keep their bits (an
+  // exact zero added to a nonzero or +0 value), and the lo products skipped altogether (PIPE)
+  // when no lane has lo_row. Every accumulator takes its hi MFMA before its lo MFMA, whether
+  // the two are interleaved by row block or run as two passes, so the bits are the same.
   // getV(mb) returns the A operand of row block mb: 8 bf16 of one head-dim row d for the key
   // slots vkey(0..7, g). Which d a (row block, lane) holds is the caller's choice; each
   // output element's dot product is the same whichever MFMA row computes it.
-  template <int NB, bool PIPE = false, class VGet>
-  __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
-    u32x4 vf = getV(0), vf1 = getV(1);   // (PIPE: in flight during the conversions)
-    u32x4 H[NB], L[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      unsigned hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = p[b][i >> 1][(2 * i) & 3], x1 = p[b][i >> 1][(2 * i + 1) & 3];
-        hi[i] = bf16_pack2(x0, x1);
-        lo[i] = bf16_pack2(x0 - bf16_lo_f(hi[i]), x1 - bf16_hi_f(hi[i]));
-      }
-      H[b] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      L[b] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    }
+  template <int NB, bool PIPE, class VGet>
+  __device__ static inline void pv_pass(f32x4 (&acc)[NB][NM], VGet& getV, const u32x4 (&P)[NB]) {
+    u32x4 vf = getV(0), vf1 = getV(1);
 #pragma unroll
     for (int mb = 0; mb < NM; ++mb) {
       // PIPE: the reads of row block mb + 2 are issued before the MFMAs of row block mb
       const u32x4 vn = mb + 2 < NM ? getV(mb + 2) : vf;
       if (PIPE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        acc[b][mb] = mma_bf16(vf, H[b], acc[b][mb]);
-        acc[b][mb] = mma_bf16(vf, L[b], acc[b][mb]);
-      }
+      for (int b = 0; b < NB; ++b) acc[b][mb] = mma_bf16(vf, P[b], acc[b][mb]);
       vf = vf1;
       vf1 = vn;
+    }
+  }
+  template <int NB, bool PIPE = false, class VGet>
+  __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4],
+                                   const bool (&lo_row)[NB], bool lo_any) {
+    u32x4 H[NB], L[NB];
+    auto make_lo = [&](int b) {
+      unsigned lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = p[b][i >> 1][(2 * i) & 3], x1 = p[b][i >> 1][(2 * i + 1) & 3];
+        const unsigned h = H[b][i];
+        lo[i] = lo_row[b] ? bf16_pack2(x0 - bf16_lo_f(h), x1 - bf16_hi_f(h)) : 0u;
+      }
+      L[b] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      unsigned hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi[i] = bf16_pack2(p[b][i >> 1][(2 * i) & 3], p[b][i >> 1][(2 * i + 1) & 3]);
+      H[b] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      if (!PIPE) make_lo(b);
+    }
+    if constexpr (PIPE) {
+      // LDS operands: the hi pass, then (only when some row needs it) the lo pass
+      pv_pass<NB, PIPE>(acc, getV, H);
+      if (lo_any) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) make_lo(b);
+        asm volatile("" ::: "memory");   // the V operands are read again, not kept
+        pv_pass<NB, PIPE>(acc, getV, L);
+      }
+    } else {
+      // register operands (an HBM-bound caller): hi and lo MFMA per row block, P_lo zero in
+      // the rows that do not need it
+#pragma unroll
+      for (int mb = 0; mb < NM; ++mb) {
+        const u32x4 vf = getV(mb);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          acc[b][mb] = mma_bf16(vf, H[b], acc[b][mb]);
+          acc[b][mb] = mma_bf16(vf, L[b], acc[b][mb]);
+        }
+      }
     }
   }
   // A operand of row block mb from raw V chunks in registers (row d = NM c + mb): slot pair
@@ -287,7 +320,8 @@ template <int D> struct Frag<float, D> {
   }
   // getV(i) returns the lane's raw V chunk (NM floats, dims NM c .. NM c + NM) of key slot i.
   template <int NB, bool PIPE = false, class VGet>
-  __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4]) {
+  __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4],
+                                   const bool (&)[NB], bool) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const VRow row = getV(i);
@@ -309,6 +343,12 @@ template <int D> struct Frag<float, D> {
 // l is kept per lane (the sum of the p values the lane holds); the row's l is the sum of its
 // four lanes' partials, taken once per split by row_l().
 constexpr float kLazy = 8.0f;
+// Precision of P in the bf16 PV product: a row at position < kLoKeys (fewer than kLoKeys + 1
+// keys, where a single bf16 P would leave errors near the tolerance) also adds the P_lo term;
+// longer rows use P_hi = bf16(p) alone, as bf16 attention kernels do. A function of the row's
+// position only, so every route makes the same choice.
+constexpr int kLoKeys = 1024;
+__device__ __forceinline__ bool needs_lo(int pos) { return pos >= 0 && pos < kLoKeys; }
 
 template <int D> struct RowState {
   static constexpr int NM = D / 16;
@@ -397,6 +437,14 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     if (SEL && pos[b] < key0) need = false;
     need_any = need_any || need;
   }
+  bool lo_row[NB];
+  bool lo_any = false;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    lo_row[b] = needs_lo(pos[b]);
+    lo_any = lo_any || lo_row[b];
+  }
+  lo_any = wave_any(lo_any);
   if (SEL) {
     f32x4 acc[NB][NM];
 #pragma unroll
@@ -404,7 +452,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb)
         acc[b][mb] = first ? f32x4{0.f, 0.f, 0.f, 0.f} : st[b].acc[mb] * alpha[b];
-    F::template pv<NB, PIPE>(acc, getV, p);
+    F::template pv<NB, PIPE>(acc, getV, p, lo_row, lo_any);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (pos[b] >= key0) {
@@ -432,7 +480,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb) accl[b][mb] = st[b].acc[mb];
-    F::template pv<NB, PIPE>(accl, getV, p);
+    F::template pv<NB, PIPE>(accl, getV, p, lo_row, lo_any);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       st[b].m = mnew[b];

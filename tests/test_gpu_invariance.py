@@ -227,3 +227,28 @@ def test_split_by_batch_variant_changes_bits():
         if B == 64:
             assert_parity(out.cpu().numpy(), oracle_out(bt), "variant parity")
     assert len(patterns) > 1
+
+
+@pytest.mark.parametrize("hq", [64, 32])
+def test_p_precision_boundary_route_invariance(hq):
+    """Rows on both sides of the position where P drops its second bf16 term (1024), also
+    inside one MFMA block (G = 8: two tokens per block): one prefill, chunks of 7 and decode
+    give identical bits, and the outputs are within the parity bar."""
+    shape = AttnShape(hq, 4, 128, 16, 256, "bf16")
+    cfg = cfg_for(shape)
+    specs = [SeqSpec(0, 1000, 60), SeqSpec(1, 1020, 9), SeqSpec(2, 1023, 2), SeqSpec(3, 10, 20),
+             SeqSpec(4, 1024, 3)]
+    _print_case("p precision boundary", hq)
+    ref, full = _chunked_route(shape, cfg, specs, 1 << 30, seed=77)
+    got, want = ref.cpu().numpy(), oracle_out(full)
+    assert_parity(got, want, "prefill across the P precision boundary")
+    # rows below position 1024 carry the second bf16 term of P: errors near 1e-6, far inside
+    # the bar that the single-term rows meet
+    pos = np.concatenate([np.arange(s.cached, s.cached + s.n_new) for s in specs])
+    short = pos < 1024
+    assert short.any() and (~short).any()
+    err_short = float(np.abs(got[short] - want[short]).max())
+    assert err_short <= 2e-5, f"rows below 1024: max-abs {err_short:.2e}"
+    for ch in (7, 1):
+        got, _ = _chunked_route(shape, cfg, specs, ch, seed=77)
+        assert_bitwise(got, ref, f"chunk {ch} vs one prefill across the P precision boundary")
