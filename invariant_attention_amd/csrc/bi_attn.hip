@@ -611,7 +611,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // past the end read kNanRows (K) and kZeroRows (V), and so do V rows at or past seq_len:
   // no stale cache bytes reach an MFMA, and a row that needs an absent page comes out NaN.
   u32x4 preK[NPF][PP], preV[NPF][PP];
-  const int last = max(nsub - 1, 0);
+  const int last = nsub - 1;   // sub-tiles past it (and every one when nsub == 0) read stand-ins
   const char* nan_rows = (const char*)&kNanRows;
   const char* zero_rows = (const char*)kZeroRows;
   // this thread's slots: row r of the sub-tile (key key0 + r, in page half r / kPage) and the
@@ -627,12 +627,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // When the rows of each slot lie in one page (a page's row chunks are a multiple of the
   // thread count), the page id and the K address are wave-uniform (scalar registers).
   constexpr bool UNI = (kPage * CHUNKS) % NT == 0;
-  auto stage_load = [&](int u, u32x4 (&pk)[PP], u32x4 (&pv)[PP]) {
+  // page id of slot k of sub-tile u (-1: none), read from the LDS ring one step before the
+  // loads that use it, so that the read's latency is not on the path of every step
+  auto page_at = [&](int u, int k) {
+    const unsigned half = UNI ? (unsigned)(k * NT / (kPage * CHUNKS)) : srow[k] / kPage;
+    const unsigned lp = 2u * (unsigned)u + half;
+    return u <= last ? lds_pages[lp % kPageCache] : -1;
+  };
+  int pgq[PP];
+  auto stage_load = [&](int u, const int (&pgs)[PP], u32x4 (&pk)[PP], u32x4 (&pv)[PP]) {
 #pragma unroll
     for (int k = 0; k < PP; ++k) {
-      const unsigned half = UNI ? (unsigned)(k * NT / (kPage * CHUNKS)) : srow[k] / kPage;
-      const unsigned lp = 2u * (unsigned)u + half;
-      int page = u <= last ? lds_pages[lp % kPageCache] : -1;
+      int page = pgs[k];
       if (UNI) page = __builtin_amdgcn_readfirstlane(page);
       const bool vin = u * kSubTile + (int)srow[k] < seq_len;
       const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
@@ -655,7 +661,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   };
 
 #pragma unroll
-  for (int i = 0; i < NPF; ++i) stage_load(i, preK[i], preV[i]);
+  for (int i = 0; i < NPF; ++i) {
+#pragma unroll
+    for (int k = 0; k < PP; ++k) pgq[k] = page_at(i, k);
+    stage_load(i, pgq, preK[i], preV[i]);
+  }
+#pragma unroll
+  for (int k = 0; k < PP; ++k) pgq[k] = page_at(NPF, k);
   for (int u0 = 0; u0 < nsub; u0 += NPF) {
 #pragma unroll
   for (int i = 0; i < NPF; ++i) {
@@ -675,7 +687,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     }
     stage_store(preK[i], preV[i]);
     __syncthreads();
-    stage_load(u + NPF, preK[i], preV[i]);
+    stage_load(u + NPF, pgq, preK[i], preV[i]);
+#pragma unroll
+    for (int k = 0; k < PP; ++k) pgq[k] = page_at(u + NPF + 1, k);
     if (wave_max >= key0) {
       const char* kt = lds_kv[0];
       const char* vt = lds_kv[1];
