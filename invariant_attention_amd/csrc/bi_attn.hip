@@ -541,7 +541,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   constexpr int CHUNKS = LD::ROWB / 16;                  // 16-byte chunks per row
   constexpr int PAIRS = kSubTile * CHUNKS;               // (row, chunk) slots of a sub-tile
   constexpr int PP = (PAIRS + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) char lds_kv[2][LD::TILE];
+  // bf16, D 128: K/V sub-tiles go from HBM straight into LDS (global_load_lds_dwordx4, 16 bytes
+  // per lane, lane i of an instruction to byte 16 i of its 1 KB block), double-buffered, in an
+  // unpadded layout whose 16-byte chunks are permuted per row (chunk lc of row R at chunk
+  // lc ^ rotl4(R % 16)) so that the K reads and the transposing V reads hit distinct banks.
+  // Otherwise the sub-tile is staged through registers into one padded buffer.
+  constexpr bool DMA = BF && D == 128 && NW == 4 && NPF == 1 && !LANESEL;
+  constexpr int DTILE = kSubTile * LD::ROWB;               // 8 KB
+  __shared__ __attribute__((aligned(16))) char lds_kv[2][DMA ? 16 : LD::TILE];
+  // the two buffers are separate variables, so the compiler can tell that the reads of one
+  // do not wait for the transfers into the other
+  __shared__ __attribute__((aligned(16))) char lds_d0[2][DMA ? DTILE : 16];   // [K, V]
+  __shared__ __attribute__((aligned(16))) char lds_d1[2][DMA ? DTILE : 16];
   __shared__ f32x4 lds_A[AREG ? 1 : NW][AREG ? 1 : NBW][AREG ? 1 : NM][64];   // [wave][block][row block][lane]
   __shared__ int lds_pages[kPageCache];
 
@@ -660,42 +671,33 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     }
   };
 
+  // DMA layout: chunk permutation of a row (rotate its 4-bit row index left by one), and this
+  // lane's byte offsets of the K operand of k-step s2 (row 16 kb + c, chunk 4 s2 + g; key block
+  // kb adds 16 rows) and of the V operand of row block x (rows rv and rv + 16, chunk
+  // 2 x + ((c & 3) >> 1), byte 8 (c & 1) in it)
+  auto rot = [](int r) { return ((r << 1) | (r >> 3)) & 15; };
+  unsigned koff[NM / 2], voff[NM];
+  const int rv = 4 * g + (c >> 2);
 #pragma unroll
-  for (int i = 0; i < NPF; ++i) {
+  for (int s2 = 0; s2 < NM / 2; ++s2) koff[s2] = c * LD::ROWB + (((4 * s2 + g) ^ rot(c)) << 4);
 #pragma unroll
-    for (int k = 0; k < PP; ++k) pgq[k] = page_at(i, k);
-    stage_load(i, pgq, preK[i], preV[i]);
-  }
-#pragma unroll
-  for (int k = 0; k < PP; ++k) pgq[k] = page_at(NPF, k);
-  for (int u0 = 0; u0 < nsub; u0 += NPF) {
-#pragma unroll
-  for (int i = 0; i < NPF; ++i) {
-    const int u = u0 + i;
-    if (u >= nsub) break;
+  for (int x = 0; x < NM; ++x)
+    voff[x] = rv * LD::ROWB + (((2 * x + ((c & 3) >> 1)) ^ rot(rv)) << 4) + 8 * (c & 1);
+  // one sub-tile step: compute sub-tile u from the K/V tile at kt / vt, then fold split j into
+  // the row state when u ends it
+  auto step = [&](int u, const char* kt, const char* vt) {
     const int key0 = u * kSubTile;
     const int j = key0 / S;
     const bool first = key0 == j * S;
     const bool last_of_split = key0 + kSubTile == (j + 1) * S || u + 1 == nsub;
-    // when the loads reach a new half of the page ring, fill the half after it; the slots
-    // it overwrites belong to pages no later load reads
-    const int lpn = (u + NPF) * (kSubTile / kPage);
-    if (RING && lpn % (kPageCache / 2) == 0 && lpn >= kPageCache / 2) {
-      const int base = lpn + kPageCache / 2;
-      for (int t = threadIdx.x; t < kPageCache / 2; t += NT)
-        if (base + t < npg_total) lds_pages[(base + t) % kPageCache] = page_of(a, b, base + t, seq_len);
-    }
-    stage_store(preK[i], preV[i]);
-    __syncthreads();
-    stage_load(u + NPF, pgq, preK[i], preV[i]);
-#pragma unroll
-    for (int k = 0; k < PP; ++k) pgq[k] = page_at(u + NPF + 1, k);
     if (wave_max >= key0) {
-      const char* kt = lds_kv[0];
-      const char* vt = lds_kv[1];
-      auto getK = [&](int kb, int s2) { return F::k_op(kt + (16 * kb + c) * LD::STRIDE, s2, g); };
+      auto getK = [&](int kb, int s2) {
+        if constexpr (DMA) return *(const u32x4*)(kt + koff[s2] + kb * 16 * LD::ROWB);
+        else return F::k_op(kt + (16 * kb + c) * LD::STRIDE, s2, g);
+      };
       auto getV = [&](int x) {
-        if constexpr (BF) return F::v_tr(vt, LD::STRIDE, x, c, g);
+        if constexpr (DMA) return F::v_tr_at(vt + voff[x], 16 * LD::ROWB);
+        else if constexpr (BF) return F::v_tr(vt, LD::STRIDE, x, c, g);
         else return F::v_row(vt + F::vkey(x, g) * LD::STRIDE, c);
       };
       if (key0 <= wave_min) {
@@ -735,7 +737,93 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
         }
       }
     }
+  };
+  // when the page-id reads reach a new half of the ring (first page lpn), fill the half after
+  // it; the slots it overwrites belong to pages no later read needs, and the end-of-step
+  // barriers order the refill against the earlier readers and the later ones
+  auto refill = [&](int lpn) {
+    if (RING && lpn % (kPageCache / 2) == 0 && lpn >= kPageCache / 2) {
+      const int base = lpn + kPageCache / 2;
+      for (int t = threadIdx.x; t < kPageCache / 2; t += NT)
+        if (base + t < npg_total) lds_pages[(base + t) % kPageCache] = page_of(a, b, base + t, seq_len);
+    }
+  };
+
+  if constexpr (DMA) {
+    // this wave's two 1 KB blocks of each tile: rows R = 8 wave + 4 t + lane / 16 (all in page
+    // half wave / 2), lane's chunk at physical position lane % 16
+    const int half = wave >> 1;
+    unsigned soff[2];
+    int srw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int R = 8 * wave + 4 * t + (lane >> 4), Rp = R & 15;
+      srw[t] = R;
+      soff[t] = Rp * LD::ROWB + (((lane & 15) ^ rot(Rp)) << 4);
+    }
+    auto pg_at = [&](int u) { return u <= last ? lds_pages[(2 * u + half) % kPageCache] : -1; };
+    auto dma = [&](int u, char (&dst)[2][DMA ? DTILE : 16], int pgv) {
+      const int page = __builtin_amdgcn_readfirstlane(pgv);
+      const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool vin = u * kSubTile + srw[t] < seq_len;
+        const char* kp = page >= 0 ? kbase + off : nan_rows;
+        const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        __builtin_amdgcn_global_load_lds((const void*)(kp + soff[t]),
+                                         (lds_ptr)&dst[0][(2 * wave + t) * 1024], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vp + soff[t]),
+                                         (lds_ptr)&dst[1][(2 * wave + t) * 1024], 16, 0, 0);
+      }
+    };
+    // (s_waitcnt vmcnt(0) alone: the tile's HBM -> LDS transfers of this wave have landed)
+    constexpr int kWaitVm0 = 0x0F70;
+    int pgn = pg_at(0);
+    dma(0, lds_d0, pgn);
+    pgn = pg_at(1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    // sub-tile u from buffer u % 2 while u + 1 lands in the other (unrolled by two, so every
+    // buffer access names its variable)
+    for (int u = 0; u < nsub; u += 2) {
+      refill(2 * (u + 2));
+      if (u + 1 < nsub) dma(u + 1, lds_d1, pgn);
+      pgn = pg_at(u + 2);
+      step(u, lds_d0[0], lds_d0[1]);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (u + 1 >= nsub) break;
+      refill(2 * (u + 3));
+      if (u + 2 < nsub) dma(u + 2, lds_d0, pgn);
+      pgn = pg_at(u + 3);
+      step(u + 1, lds_d1[0], lds_d1[1]);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) {
+#pragma unroll
+    for (int k = 0; k < PP; ++k) pgq[k] = page_at(i, k);
+    stage_load(i, pgq, preK[i], preV[i]);
+  }
+#pragma unroll
+  for (int k = 0; k < PP; ++k) pgq[k] = page_at(NPF, k);
+  for (int u0 = 0; u0 < nsub; u0 += NPF) {
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) {
+    const int u = u0 + i;
+    if (u >= nsub) break;
+    refill((u + NPF) * (kSubTile / kPage));
+    stage_store(preK[i], preV[i]);
+    __syncthreads();
+    stage_load(u + NPF, pgq, preK[i], preV[i]);
+#pragma unroll
+    for (int k = 0; k < PP; ++k) pgq[k] = page_at(u + NPF + 1, k);
+    step(u, lds_kv[0], lds_kv[1]);
+    __syncthreads();
+  }
   }
   }
   // Epilogue: out = A / L for every valid row.

@@ -247,6 +247,16 @@ template <int D> struct Frag<__bf16, D> {
   // k = 0..3; so when lane j names dims [16 mb + 4 (j % 4), +4) of key KEY(j / 4), lane c
   // receives dim 16 mb + c of keys KEY(0..3). KEY(k) = 4 g + k gives slots 0..3 and
   // 16 + 4 g + k slots 4..7, the keys the score layout left in this lane group.
+  // The same two transposing reads at a precomputed lane address p (the first 16 keys' row)
+  // and p + gap (the row 16 keys later), for swizzled tile layouts.
+  __device__ static inline u32x4 v_tr_at(const char* p, int gap) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + gap));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+  }
   __device__ static inline u32x4 v_tr(const char* vt, int stride, int mb, int c, int g) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
