@@ -543,8 +543,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   constexpr int PP = (PAIRS + NT - 1) / NT;
   // bf16, D 128: K/V sub-tiles go from HBM straight into LDS (global_load_lds_dwordx4, 16 bytes
   // per lane, lane i of an instruction to byte 16 i of its 1 KB block), double-buffered, in an
-  // unpadded layout whose 16-byte chunks are permuted per row (chunk lc of row R at chunk
-  // lc ^ rotl4(R % 16)) so that the K reads and the transposing V reads hit distinct banks.
+  // unpadded layout whose 16-byte chunks are rotated per row (chunk lc of row R at chunk
+  // (lc + 2 R) % 16): the same banks as a 32-byte row padding, which the K reads and the
+  // transposing V reads use without conflicts.
   // Otherwise the sub-tile is staged through registers into one padded buffer.
   constexpr bool DMA = BF && D == 128 && NW == 4 && NPF == 1 && !LANESEL;
   constexpr int DTILE = kSubTile * LD::ROWB;               // 8 KB
@@ -671,18 +672,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     }
   };
 
-  // DMA layout: chunk permutation of a row (rotate its 4-bit row index left by one), and this
-  // lane's byte offsets of the K operand of k-step s2 (row 16 kb + c, chunk 4 s2 + g; key block
-  // kb adds 16 rows) and of the V operand of row block x (rows rv and rv + 16, chunk
-  // 2 x + ((c & 3) >> 1), byte 8 (c & 1) in it)
-  auto rot = [](int r) { return ((r << 1) | (r >> 3)) & 15; };
+  // DMA layout: physical chunk of logical chunk lc in row R, and this lane's byte offsets of the
+  // K operand of k-step s2 (row 16 kb + c, chunk 4 s2 + g; key block kb adds 16 rows) and of
+  // the V operand of row block x (rows rv and rv + 16, chunk 2 x + ((c & 3) >> 1), byte
+  // 8 (c & 1) in it)
+  auto pchunk = [](int lc, int R) { return (lc + 2 * R) & 15; };
   unsigned koff[NM / 2], voff[NM];
   const int rv = 4 * g + (c >> 2);
 #pragma unroll
-  for (int s2 = 0; s2 < NM / 2; ++s2) koff[s2] = c * LD::ROWB + (((4 * s2 + g) ^ rot(c)) << 4);
+  for (int s2 = 0; s2 < NM / 2; ++s2) koff[s2] = c * LD::ROWB + (pchunk(4 * s2 + g, c) << 4);
 #pragma unroll
   for (int x = 0; x < NM; ++x)
-    voff[x] = rv * LD::ROWB + (((2 * x + ((c & 3) >> 1)) ^ rot(rv)) << 4) + 8 * (c & 1);
+    voff[x] = rv * LD::ROWB + (pchunk(2 * x + ((c & 3) >> 1), rv) << 4) + 8 * (c & 1);
   // one sub-tile step: compute sub-tile u from the K/V tile at kt / vt, then fold split j into
   // the row state when u ends it
   auto step = [&](int u, const char* kt, const char* vt) {
@@ -759,7 +760,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     for (int t = 0; t < 2; ++t) {
       const int R = 8 * wave + 4 * t + (lane >> 4), Rp = R & 15;
       srw[t] = R;
-      soff[t] = Rp * LD::ROWB + (((lane & 15) ^ rot(Rp)) << 4);
+      soff[t] = Rp * LD::ROWB + (((lane - 2 * Rp) & 15) << 4);   // logical chunk of physical lane % 16
     }
     auto pg_at = [&](int u) { return u <= last ? lds_pages[(2 * u + half) % kPageCache] : -1; };
     auto dma = [&](int u, char (&dst)[2][DMA ? DTILE : 16], int pgv) {
