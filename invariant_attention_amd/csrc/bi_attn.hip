@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
 // a wave owns 64 FPL consecutive floats of that block (lane: FPL floats of one row), folds them
 // over the splits in ascending j and writes A / L. The accumulator loads run U splits ahead of
 // the fold in a ring of U register slots (slot u holds split j with j % U == u; a slot is
-// refilled as soon as it is folded), the first U before the row's split count is known. Loads
+// refilled as soon as it is folded), the first few before the row's split count is known. Loads
 // past the last split re-read it and are not folded, so every step issues the same loads.
 // With one float per lane a wave covers part of one row, and the (m, l) pairs of 64 splits
 // come in one load (lane i: split j0 + i), read out with readlane; with four floats per lane
@@ -380,22 +380,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
   const int seq_len = a.seq_lens[b];
   float2 mlj[WIN ? 1 : U], mlw = {0.f, 0.f}, mlw_next = {0.f, 0.f};
   V accj[U];
-  if (WIN) {
-    mlw = ml[min(lane, a.jmax - 1) * ml_step];
-    mlw_next = ml[min(64 + lane, a.jmax - 1) * ml_step];
-  }
+  // the first kEarly loads go out with the length's; the rest of the ring once the row's split
+  // count J is known (clamped to its last split, so no load reads another row's slots)
+  constexpr int kEarly = 4;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kEarly; ++u) {
     const int jj = min(u, a.jmax - 1);
     if (!WIN) mlj[u] = ml[jj * ml_step];
     accj[u] = *(const V*)(acc + jj * acc_step);
   }
-  if (seq_len <= 0 || seq_len > a.max_seq_len) {
+  const bool bad = seq_len <= 0 || seq_len > a.max_seq_len;
+  const int J = bad ? 1 : (seq_len - 1) / split_len(a, seq_len) + 1;
+  if (WIN) {
+    mlw = ml[min(lane, J - 1) * ml_step];
+    mlw_next = ml[min(64 + lane, J - 1) * ml_step];
+  }
+#pragma unroll
+  for (int u = kEarly; u < U; ++u) {
+    const int jj = min(u, J - 1);
+    if (!WIN) mlj[u] = ml[jj * ml_step];
+    accj[u] = *(const V*)(acc + jj * acc_step);
+  }
+  if (bad) {
 #pragma unroll
     for (int e = 0; e < FPL; ++e) o[e] = __builtin_nanf("");
     return;
   }
-  const int J = (seq_len - 1) / split_len(a, seq_len) + 1;
   float M = 0.f, L = 0.f;
   float A[FPL];
 #pragma unroll
