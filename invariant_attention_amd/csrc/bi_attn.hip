@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
     for (int e = 0; e < FPL; ++e) o[e] = __builtin_nanf("");
     return;
   }
-  float M = 0.f, L = 0.f;
+  float M = -__builtin_inff(), L = 0.f;
   float A[FPL];
 #pragma unroll
   for (int e = 0; e < FPL; ++e) A[e] = 0.f;
@@ -419,7 +419,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < J) {
-        const bool first = (j0 + u) == 0;
         float m, l;
         if (WIN) {
           m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mw.x), u));
@@ -429,14 +428,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
           l = mlj[WIN ? 0 : u].y;
         }
         float fa, fb;
-        fold_scalars(M, L, m, l, first, fa, fb);
+        fold_scalars(M, L, m, l, fa, fb);
         const V x = accj[u];
 #pragma unroll
         for (int e = 0; e < FPL; ++e) {
           float xe;
           if constexpr (FPL == 1) xe = x;
           else xe = x[e];
-          A[e] = fold_elem(A[e], xe, fa, fb, first);
+          A[e] = fold_elem(A[e], xe, fa, fb);
         }
       }
       const int jn = min(j0 + u + U, J - 1);
@@ -613,8 +612,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     } else {
       F::zero_q(qf[cb]);
     }
-    Mrow[cb] = 0.f;
+    Mrow[cb] = -__builtin_inff();
     Lrow[cb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < NM; ++mb) Areg[AREG ? cb : 0][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int nsub = bad_seq ? 0 : (pos_max_wg + kSubTile) / kSubTile;
@@ -733,16 +734,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
         if (blk_max[cb] < j * S) continue;
         const bool act = pos_c[cb] >= j * S;
         float M = Mrow[cb], L = Lrow[cb], fa, fb;
-        fold_scalars(M, L, st[cb].m, row_l(st[cb]), j == 0, fa, fb);
+        fold_scalars(M, L, st[cb].m, row_l(st[cb]), fa, fb);
         if (act) {
           Mrow[cb] = M;
           Lrow[cb] = L;
 #pragma unroll
           for (int mb = 0; mb < NM; ++mb) {
             f32x4& slot = AREG ? Areg[AREG ? cb : 0][mb] : lds_A[AREG ? 0 : wave][AREG ? 0 : cb][AREG ? 0 : mb][lane];
-            f32x4 A = j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot;
+            f32x4 A = (AREG || j > 0) ? slot : f32x4{0.f, 0.f, 0.f, 0.f};   // (LDS slots start unwritten)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb, j == 0);
+            for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb);
             slot = A;
           }
         }

@@ -503,21 +503,18 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 
 // Ascending fold of split j's state into the row state (the same function the combine kernel
 // applies element by element): M' = max(M, m), a = 2^(M - M'), b = 2^(m - M'),
-// L = L a + l b, A = A a + acc b, with split 0 copied as is.
-__device__ __forceinline__ void fold_scalars(float& M, float& L, float m, float l, bool first,
-                                             float& a, float& b) {
-  if (first) {
-    M = m; L = l; a = 0.f; b = 1.f;
-    return;
-  }
+// L = L a + l b, A = A a + acc b. The row state starts at (M, L, A) = (-inf, 0, 0), so split 0
+// gives a = 0, b = 1 and copies its state exactly (l b = l, acc b = acc, 0 a + x = x for the
+// never negative-zero partials) with no special case.
+__device__ __forceinline__ void fold_scalars(float& M, float& L, float m, float l, float& a, float& b) {
   const float Mn = fmaxf(M, m);
   a = ex2(M - Mn);
   b = ex2(m - Mn);
   L = __builtin_fmaf(L, a, l * b);
   M = Mn;
 }
-__device__ __forceinline__ float fold_elem(float A, float acc, float a, float b, bool first) {
-  return first ? acc : __builtin_fmaf(A, a, acc * b);
+__device__ __forceinline__ float fold_elem(float A, float acc, float a, float b) {
+  return __builtin_fmaf(A, a, acc * b);
 }
 
 }  // namespace bi
