@@ -557,7 +557,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // transposing V reads use without conflicts.
   // Otherwise the sub-tile is staged through registers into one padded buffer.
   constexpr bool DMA = BF && D == 128 && NW == 4 && NPF == 1 && !LANESEL;
-  constexpr int DTILE = kSubTile * LD::ROWB;               // 8 KB
+  constexpr int KPS = 2;                                   // sub-tiles per DMA step
+  constexpr int DTILE = KPS * kSubTile * LD::ROWB;         // 16 KB: 64 keys
   __shared__ __attribute__((aligned(16))) char lds_kv[2][DMA ? 16 : LD::TILE];
   // the two buffers are separate variables, so the compiler can tell that the reads of one
   // do not wait for the transfers into the other
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     voff[x] = rv * LD::ROWB + (pchunk(2 * x + ((c & 3) >> 1), rv) << 4) + 8 * (c & 1);
   // one sub-tile step: compute sub-tile u from the K/V tile at kt / vt, then fold split j into
   // the row state when u ends it
-  auto step = [&](int u, const char* kt, const char* vt) {
+  auto step = [&](int u, const char* kt, const char* vt) __attribute__((always_inline)) {
     const int key0 = u * kSubTile;
     const int j = key0 / S;
     const bool first = key0 == j * S;
@@ -762,54 +763,62 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   };
 
   if constexpr (DMA) {
-    // this wave's two 1 KB blocks of each tile: rows R = 8 wave + 4 t + lane / 16 (all in page
-    // half wave / 2), lane's chunk at physical position lane % 16
-    const int half = wave >> 1;
-    unsigned soff[2];
-    int srw[2];
+    // A step covers KPS = 2 sub-tiles (64 keys, 4 pages). This wave's four 1 KB blocks of each
+    // step's tile: rows R = 16 wave + 4 t + lane / 16 (page `wave` of the step), lane's chunk at
+    // physical position lane % 16.
+    unsigned soff[4];
+    int srw[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int R = 8 * wave + 4 * t + (lane >> 4), Rp = R & 15;
+    for (int t = 0; t < 4; ++t) {
+      const int R = 16 * wave + 4 * t + (lane >> 4), Rp = R & 15;
       srw[t] = R;
       soff[t] = Rp * LD::ROWB + (((lane - 2 * Rp) & 15) << 4);   // logical chunk of physical lane % 16
     }
-    auto pg_at = [&](int u) { return u <= last ? lds_pages[(2 * u + half) % kPageCache] : -1; };
-    auto dma = [&](int u, char (&dst)[2][DMA ? DTILE : 16], int pgv) {
+    // page of step sp read by this wave (logical page 4 sp + wave, in sub-tile 2 sp + wave / 2)
+    auto pg_at = [&](int sp) {
+      return 2 * sp + (wave >> 1) <= last ? lds_pages[(4 * sp + wave) % kPageCache] : -1;
+    };
+    auto dma = [&](int sp, char (&dst)[2][DMA ? DTILE : 16], int pgv) __attribute__((always_inline)) {
       const int page = __builtin_amdgcn_readfirstlane(pgv);
       const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bool vin = u * kSubTile + srw[t] < seq_len;
+      for (int t = 0; t < 4; ++t) {
+        const bool vin = sp * KPS * kSubTile + srw[t] < seq_len;
         const char* kp = page >= 0 ? kbase + off : nan_rows;
         const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
         typedef __attribute__((address_space(3))) void* lds_ptr;
         __builtin_amdgcn_global_load_lds((const void*)(kp + soff[t]),
-                                         (lds_ptr)&dst[0][(2 * wave + t) * 1024], 16, 0, 0);
+                                         (lds_ptr)&dst[0][(4 * wave + t) * 1024], 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(vp + soff[t]),
-                                         (lds_ptr)&dst[1][(2 * wave + t) * 1024], 16, 0, 0);
+                                         (lds_ptr)&dst[1][(4 * wave + t) * 1024], 16, 0, 0);
       }
+    };
+    auto steps = [&](int sp, char (&buf)[2][DMA ? DTILE : 16]) __attribute__((always_inline)) {
+      step(KPS * sp, buf[0], buf[1]);
+      if (KPS * sp + 1 < nsub) step(KPS * sp + 1, buf[0] + kSubTile * LD::ROWB, buf[1] + kSubTile * LD::ROWB);
     };
     // (s_waitcnt vmcnt(0) alone: the tile's HBM -> LDS transfers of this wave have landed)
     constexpr int kWaitVm0 = 0x0F70;
+    const int nst = (nsub + KPS - 1) / KPS;
     int pgn = pg_at(0);
     dma(0, lds_d0, pgn);
     pgn = pg_at(1);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    // sub-tile u from buffer u % 2 while u + 1 lands in the other (unrolled by two, so every
+    // step sp from buffer sp % 2 while sp + 1 lands in the other (unrolled by two, so every
     // buffer access names its variable)
-    for (int u = 0; u < nsub; u += 2) {
-      refill(2 * (u + 2));
-      if (u + 1 < nsub) dma(u + 1, lds_d1, pgn);
-      pgn = pg_at(u + 2);
-      step(u, lds_d0[0], lds_d0[1]);
+    for (int sp = 0; sp < nst; sp += 2) {
+      refill(4 * (sp + 2));
+      if (sp + 1 < nst) dma(sp + 1, lds_d1, pgn);
+      pgn = pg_at(sp + 2);
+      steps(sp, lds_d0);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      if (u + 1 >= nsub) break;
-      refill(2 * (u + 3));
-      if (u + 2 < nsub) dma(u + 2, lds_d0, pgn);
-      pgn = pg_at(u + 3);
-      step(u + 1, lds_d1[0], lds_d1[1]);
+      if (sp + 1 >= nst) break;
+      refill(4 * (sp + 3));
+      if (sp + 2 < nst) dma(sp + 2, lds_d0, pgn);
+      pgn = pg_at(sp + 3);
+      steps(sp + 1, lds_d1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
     }

@@ -13,7 +13,8 @@ import torch
 import invariant_attention_amd as bi
 from synth import CONFIG_SHAPES, AttnShape, SeqSpec, build_batch
 from gpu_harness import (assert_bitwise, assert_parity, bits, cfg_for, decode_workspace,
-                         oracle_out, page_update, run_decode, run_prefill, to_device)
+                         oracle_out, oracle_rows, page_update, run_decode, run_prefill,
+                         to_device)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -252,3 +253,23 @@ def test_p_precision_boundary_route_invariance(hq):
     for ch in (7, 1):
         got, _ = _chunked_route(shape, cfg, specs, ch, seed=77)
         assert_bitwise(got, ref, f"chunk {ch} vs one prefill across the P precision boundary")
+
+
+@pytest.mark.parametrize("hq", [64, 32])
+def test_prefill_past_page_id_ring(hq):
+    """Sequences longer than the prefill kernel's LDS ring of 2048 page ids (32768 tokens), so
+    the ring is refilled while the tile runs: a 40000-token prefix with a 70-token chunk and
+    a shorter neighbour. One prefill, chunks of 16 and decode give identical bits; sampled rows
+    match the oracle."""
+    shape = AttnShape(hq, 4, 128, 16, 256, "bf16")
+    cfg = cfg_for(shape)
+    specs = [SeqSpec(0, 40000, 70), SeqSpec(1, 33000, 5)]
+    _print_case("ring", hq)
+    ref, full = _chunked_route(shape, cfg, specs, 1 << 30, seed=91)
+    for ch in (16, 1):
+        got, _ = _chunked_route(shape, cfg, specs, ch, seed=91)
+        assert_bitwise(got, ref, f"chunk {ch} vs one prefill past the page-id ring")
+    rows = [(t, h) for t in (0, 37, 69, 70, 74) for h in (0, hq // 2 + 3, hq - 1)]
+    want = oracle_rows(full, rows)
+    got = np.stack([ref[t, h].cpu().numpy() for t, h in rows])
+    assert_parity(got, want, "prefill rows past the page-id ring")
