@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
       if constexpr (std::is_same<E, float>::value) return buf.v[x];
       else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
     };
-    subtile_step<E, D, NB, false>(st, qf, posv, getK, getV, a.cscale, key0, g, u.w0 + t == 0,
+    subtile_step<E, D, NB>(st, qf, posv, getK, getV, a.cscale, key0, g, u.w0 + t == 0,
                                   key0 + kSubTile - 1 > pos);
   };
   // Every sub-tile of unit u, its first one already in flight in b0. Even sub-tiles are
@@ -539,7 +539,7 @@ __device__ bool pf_item(const AttnParams& a, int tq, int i, int& ob, int& otile)
   return false;
 }
 
-template <typename E, int D, int NBW, int NW, bool LANESEL, bool RING, int NPF, bool AREG, int MINB>
+template <typename E, int D, int NBW, int NW, bool RING, int NPF, bool AREG, int MINB>
 __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   using F = Frag<E, D>;
   using LD = Lds<D, E>;
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // (lc + 2 R) % 16): the same banks as a 32-byte row padding, which the K reads and the
   // transposing V reads use without conflicts.
   // Otherwise the sub-tile is staged through registers into one padded buffer.
-  constexpr bool DMA = BF && D == 128 && NW == 4 && NPF == 1 && !LANESEL;
+  constexpr bool DMA = BF && D == 128 && NW == 4 && NPF == 1;
   constexpr int KPS = 2;                                   // sub-tiles per DMA step
   constexpr int DTILE = KPS * kSubTile * LD::ROWB;         // 16 KB: 64 keys
   __shared__ __attribute__((aligned(16))) char lds_kv[2][DMA ? 16 : LD::TILE];
@@ -713,19 +713,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
         else if constexpr (BF) return F::v_tr(vt, LD::STRIDE, x, c, g);
         else return F::v_row(vt + F::vkey(x, g) * LD::STRIDE, c);
       };
-      if (key0 <= wave_min) {
-        // every valid row of the wave reaches key0: all blocks advance together
-        subtile_step<E, D, NBW, false, BF>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
-                                       key0 + kSubTile - 1 > wave_min);
-      } else {
-        // some row stops before key0 (the diagonal of the tile): block by block, and row by
-        // row inside a block when a block holds several tokens (G < 16)
-#pragma unroll
-        for (int cb = 0; cb < NBW; ++cb)
-          if (blk_max[cb] >= key0)
-            subtile_step<E, D, 1, LANESEL, BF>(&st[cb], &qf[cb], &pos_c[cb], getK, getV, a.cscale,
-                                           key0, g, first, true);
-      }
+      // all blocks advance together; on the diagonal of the tile the mask leaves rows whose
+      // position is below key0 as they are (see subtile_step)
+      subtile_step<E, D, NBW, BF>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
+                                  key0 + kSubTile - 1 > wave_min);
     }
     if (last_of_split && wave_max >= j * S) {
       // fold split j into every row whose position reaches it (also when this wave's rows
@@ -1113,13 +1104,8 @@ int launch_prefill(const AttnParams& a, hipStream_t s) {
   const int64_t wgs = (int64_t)((a.max_q_len + tq - 1) / tq) * a.batch * a.hkv;
   if (wgs > 0x7fffffff) return BI_EUNSUPPORTED;
   const dim3 grid((unsigned)wgs);
-  if (a.group >= 16) {
-    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, true, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
-    else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, false, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
-  } else {
-    if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, true, true, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
-    else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, true, false, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
-  }
+  if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, true, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
+  else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
   return launched();
 }
 

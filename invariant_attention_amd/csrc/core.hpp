@@ -375,10 +375,12 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 //   pos[b]        -> this lane's row position in block b
 //   first: first sub-tile of the split (state reset, not rescaled)
 //   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
-//   SEL:   rows with pos < key0 keep their state (only when a block mixes such rows)
+//   A row with pos < key0 (all its keys masked) takes p = 0 everywhere, which leaves its state
+//   bitwise as it was, except at a split start, where it gets a meaningless state for a split
+//   it never folds (pos < key0 = the split's first key).
 //   PIPE:  operand reads are issued ahead of the MFMAs that use them (LDS operands): K one
 //          k-step ahead, V two row blocks ahead
-template <typename E, int D, int NB, bool SEL, bool PIPE = false, class KGet, class VGet>
+template <typename E, int D, int NB, bool PIPE = false, class KGet, class VGet>
 __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Frag<E, D>::Q* q,
                                              const int* pos, KGet&& getK, VGet&& getV,
                                              float cscale, int key0, int g, bool first,
@@ -444,7 +446,6 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
                      ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
     lnew[b] = first ? rs : __builtin_fmaf(st[b].l, alpha[b], rs);
-    if (SEL && pos[b] < key0) need = false;
     need_any = need_any || need;
   }
   bool lo_row[NB];
@@ -455,49 +456,30 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     lo_any = lo_any || lo_row[b];
   }
   lo_any = wave_any(lo_any);
-  if (SEL) {
-    f32x4 acc[NB][NM];
+  if (first) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int mb = 0; mb < NM; ++mb)
-        acc[b][mb] = first ? f32x4{0.f, 0.f, 0.f, 0.f} : st[b].acc[mb] * alpha[b];
-    F::template pv<NB, PIPE>(acc, getV, p, lo_row, lo_any);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (pos[b] >= key0) {
-        st[b].m = mnew[b];
-        st[b].l = lnew[b];
-#pragma unroll
-        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = acc[b][mb];
-      }
-    }
-  } else {
-    if (first) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else if (wave_any(need_any)) {
-      // alpha == 1 exactly for rows that kept their reference, so x * alpha == x
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
-    }
-    f32x4 accl[NB][NM];
+      for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (wave_any(need_any)) {
+    // alpha == 1 exactly for rows that kept their reference, so x * alpha == x
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int mb = 0; mb < NM; ++mb) accl[b][mb] = st[b].acc[mb];
-    F::template pv<NB, PIPE>(accl, getV, p, lo_row, lo_any);
+      for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
+  }
+  f32x4 accl[NB][NM];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      st[b].m = mnew[b];
-      st[b].l = lnew[b];
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = accl[b][mb];
-    }
+    for (int mb = 0; mb < NM; ++mb) accl[b][mb] = st[b].acc[mb];
+  F::template pv<NB, PIPE>(accl, getV, p, lo_row, lo_any);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    st[b].m = mnew[b];
+    st[b].l = lnew[b];
+#pragma unroll
+    for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = accl[b][mb];
   }
 }
 
