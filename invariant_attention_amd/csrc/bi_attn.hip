@@ -139,8 +139,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
     return (len > 0 && len <= a.max_seq_len) ? (len - 1) / split_len(a, len) + 1 : 0;
   };
   // Items in two runs: first every split but the last of each sequence (b, then j), then the
-  // last split of each sequence (b). A last split is the only one that can be short, so the
-  // items handed out last (to the waves that get one more) are the cheap ones.
+  // last split of each sequence. A last split is the only one that can be short, so the items
+  // handed out last (to the waves that get one more) are the cheap ones.
   int total_full = 0, total_last = 0;
   for (int cb = 0; cb < a.batch; cb += 64) {
     const int nj = splits_of(chunk_len(cb));
@@ -170,6 +170,37 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
     const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(before + incl <= k));
     return nb;
   };
+  // With a fixed split size the last run is ordered by the last split's sub-tile count,
+  // largest first (ties by sequence): the waves that get one item more get the cheapest.
+  const bool by_cost = a.policy == BI_SPLIT_FIXED;
+  const int cmax = (a.split + kSubTile - 1) / kSubTile;
+  auto last_cost = [&](int len) {
+    const int nj = splits_of(len);
+    return nj > 0 ? (len - (nj - 1) * a.split + kSubTile - 1) / kSubTile : 0;
+  };
+  // sequence of the k-th last split in (cost descending, sequence) order
+  auto last_by_cost = [&](int k) {
+    for (int cst = cmax; cst >= 1; --cst) {
+      int cnt = 0;
+      for (int cb = 0; cb < a.batch; cb += 64) cnt += wave_sum_i(last_cost(chunk_len(cb)) == cst ? 1 : 0);
+      cnt = __builtin_amdgcn_readfirstlane(cnt);
+      if (k >= cnt) {
+        k -= cnt;
+        continue;
+      }
+      for (int cb = 0;; cb += 64) {
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(last_cost(chunk_len(cb)) == cst);
+        const int n = __builtin_popcountll(m);
+        if (k < n) {
+          unsigned long long mm = m;
+          for (int t = 0; t < k; ++t) mm &= mm - 1;   // drop the k lowest set lanes
+          return cb + (int)__builtin_ctzll(mm);
+        }
+        k -= n;
+      }
+    }
+    return 0;   // not reached: k < total_last
+  };
   auto locate = [&](int i, int& ob, int& oj, int& olen) {
     if (i < total_full) {
       const int nb = seek(0, i, cb0, before0, incl0);
@@ -177,8 +208,12 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
       oj = i - before0 - (nb > 0 ? __builtin_amdgcn_readlane(incl0, nb - 1) : 0);
       olen = a.seq_lens[ob];   // uniform: a scalar load, which leaves the vector loads in flight
     } else {
-      const int nb = seek(1, i - total_full, cb1, before1, incl1);
-      ob = cb1 + nb;
+      if (by_cost) {
+        ob = __builtin_amdgcn_readfirstlane(last_by_cost(i - total_full));
+      } else {
+        const int nb = seek(1, i - total_full, cb1, before1, incl1);
+        ob = cb1 + nb;
+      }
       olen = a.seq_lens[ob];
       oj = splits_of(olen) - 1;
     }
