@@ -602,7 +602,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   __shared__ f32x4 lds_A[AREG ? 1 : NW][AREG ? 1 : NBW][AREG ? 1 : NM][64];   // [wave][block][row block][lane]
   __shared__ int lds_pages[kPageCache];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int G = a.group;
   const int tq = COLS / G;                       // tokens per tile (G divides COLS)
@@ -754,25 +754,22 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
                                   key0 + kSubTile - 1 > wave_min);
     }
     if (last_of_split && wave_max >= j * S) {
-      // fold split j into every row whose position reaches it (also when this wave's rows
-      // ended before this last sub-tile of the split)
+      // fold split j into the rows of every block that reaches it (also when this wave's rows
+      // ended before this last sub-tile of the split). A row whose position is below the
+      // split's first key holds the empty state there, which the fold leaves as it was, so
+      // every lane folds.
 #pragma unroll
       for (int cb = 0; cb < NBW; ++cb) {
         if (blk_max[cb] < j * S) continue;
-        const bool act = pos_c[cb] >= j * S;
-        float M = Mrow[cb], L = Lrow[cb], fa, fb;
-        fold_scalars(M, L, st[cb].m, row_l(st[cb]), fa, fb);
-        if (act) {
-          Mrow[cb] = M;
-          Lrow[cb] = L;
+        float fa, fb;
+        fold_scalars(Mrow[cb], Lrow[cb], st[cb].m, row_l(st[cb]), fa, fb);
 #pragma unroll
-          for (int mb = 0; mb < NM; ++mb) {
-            f32x4& slot = AREG ? Areg[AREG ? cb : 0][mb] : lds_A[AREG ? 0 : wave][AREG ? 0 : cb][AREG ? 0 : mb][lane];
-            f32x4 A = (AREG || j > 0) ? slot : f32x4{0.f, 0.f, 0.f, 0.f};   // (LDS slots start unwritten)
+        for (int mb = 0; mb < NM; ++mb) {
+          f32x4& slot = AREG ? Areg[AREG ? cb : 0][mb] : lds_A[AREG ? 0 : wave][AREG ? 0 : cb][AREG ? 0 : mb][lane];
+          f32x4 A = (AREG || j > 0) ? slot : f32x4{0.f, 0.f, 0.f, 0.f};   // (LDS slots start unwritten)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb);
-            slot = A;
-          }
+          for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb);
+          slot = A;
         }
       }
     }

@@ -376,8 +376,8 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 //   first: first sub-tile of the split (state reset, not rescaled)
 //   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
 //   A row with pos < key0 (all its keys masked) takes p = 0 everywhere, which leaves its state
-//   bitwise as it was, except at a split start, where it gets a meaningless state for a split
-//   it never folds (pos < key0 = the split's first key).
+//   bitwise as it was; at a split start it gets the empty state (m = -inf, l = 0, acc = 0),
+//   which the ascending fold leaves bitwise unchanged (a = 1, b = 0).
 //   PIPE:  operand reads are issued ahead of the MFMAs that use them (LDS operands): K one
 //          k-step ahead, V two row blocks ahead
 template <typename E, int D, int NB, bool PIPE = false, class KGet, class VGet>
@@ -438,7 +438,8 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     } else {
       mnew[b] = st[b].m;
     }
-    const float nm = -mnew[b];
+    // (an all-masked row has mnew = -inf: the offset -FLT_MAX keeps its p = 2^-inf = 0)
+    const float nm = -__builtin_fmaxf(mnew[b], -3.40282347e38f);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -485,18 +486,20 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 
 // Ascending fold of split j's state into the row state (the same function the combine kernel
 // applies element by element): M' = max(M, m), a = 2^(M - M'), b = 2^(m - M'),
-// L = L a + l b, A = A a + acc b. The row state starts at (M, L, A) = (-inf, 0, 0), so split 0
-// gives a = 0, b = 1 and copies its state exactly (l b = l, acc b = acc, 0 a + x = x for the
-// never negative-zero partials) with no special case.
+// L = l b + L a, A = acc b + A a, each one fma with the rounded product of the row state as
+// addend (so A can be updated in place). The row state starts at (M, L, A) = (-inf, 0, 0), so
+// split 0 gives a = 0, b = 1 and copies its state exactly (x 1 + 0 = x for the never
+// negative-zero partials) with no special case; an empty split (m = -inf, l = 0, acc = 0)
+// gives a = 1, b = 0 and leaves the row state as it was.
 __device__ __forceinline__ void fold_scalars(float& M, float& L, float m, float l, float& a, float& b) {
   const float Mn = fmaxf(M, m);
   a = ex2(M - Mn);
   b = ex2(m - Mn);
-  L = __builtin_fmaf(L, a, l * b);
+  L = __builtin_fmaf(l, b, L * a);
   M = Mn;
 }
 __device__ __forceinline__ float fold_elem(float A, float acc, float a, float b) {
-  return __builtin_fmaf(A, a, acc * b);
+  return __builtin_fmaf(acc, b, A * a);
 }
 
 }  // namespace bi
