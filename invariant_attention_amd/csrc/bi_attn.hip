@@ -658,8 +658,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // page ids of the logical pages the tile reads, in an LDS ring of kPageCache entries
   // (logical page lp in slot lp % kPageCache), refilled half a ring ahead of use
   const int npg_total = nsub * (kSubTile / kPage);
-  for (int i = threadIdx.x; i < min(npg_total, kPageCache); i += NT) lds_pages[i] = page_of(a, b, i, seq_len);
-  __syncthreads();
+  if constexpr (!DMA) {
+    for (int i = threadIdx.x; i < min(npg_total, kPageCache); i += NT) lds_pages[i] = page_of(a, b, i, seq_len);
+    __syncthreads();
+  }
 
   // staging: each thread owns the same (row, 16-byte chunk) slots of the K and V sub-tiles
   const char* kbase = a.k_cache + kvh * head_stride;
@@ -797,23 +799,47 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
       srw[t] = R;
       soff[t] = Rp * LD::ROWB + (((lane - 2 * Rp) & 15) << 4);   // logical chunk of physical lane % 16
     }
-    // page of step sp read by this wave (logical page 4 sp + wave, in sub-tile 2 sp + wave / 2)
-    auto pg_at = [&](int sp) {
-      return 2 * sp + (wave >> 1) <= last ? lds_pages[(4 * sp + wave) % kPageCache] : -1;
+    // Page ids: lane i of pg_cur holds the page this wave reads in step pbase + i (logical page
+    // 4 (pbase + i) + wave, in sub-tile 2 (pbase + i) + wave / 2; -1 when that sub-tile is past
+    // the last one or the page must not be read), pg_nxt the next 64 steps' ids; a step takes
+    // its id with one readlane, so no memory wait sits between the steps' loads.
+    auto pg_batch = [&](int base) {
+      const int sp = base + lane;
+      const int p = page_of_nb(a, b, 4 * sp + wave, seq_len);
+      return 2 * sp + (wave >> 1) <= last ? p : -1;
     };
-    auto dma = [&](int sp, char (&dst)[2][DMA ? DTILE : 16], int pgv) __attribute__((always_inline)) {
-      const int page = __builtin_amdgcn_readfirstlane(pgv);
+    int pbase = 0;
+    int pg_cur = pg_batch(0), pg_nxt = pg_batch(64);
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    typedef const __attribute__((address_space(1))) char* gptr;
+    auto dma = [&](int sp, char (&dst)[2][DMA ? DTILE : 16]) __attribute__((always_inline)) {
+      const int page = __builtin_amdgcn_readlane(pg_cur, sp - pbase);
+      if (sp - pbase == 63) {
+        pbase += 64;
+        pg_cur = pg_nxt;
+        pg_nxt = pg_batch(pbase + 64);
+      }
       const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
+      if (page >= 0 && (4 * sp + wave + 1) * kPage <= seq_len) {
+        // the whole page lies before seq_len: one scalar base per page, lane offsets
+        const gptr kp = (gptr)(kbase + off), vp = (gptr)(vbase + off);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bool vin = sp * KPS * kSubTile + srw[t] < seq_len;
-        const char* kp = page >= 0 ? kbase + off : nan_rows;
-        const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
-        typedef __attribute__((address_space(3))) void* lds_ptr;
-        __builtin_amdgcn_global_load_lds((const void*)(kp + soff[t]),
-                                         (lds_ptr)&dst[0][(4 * wave + t) * 1024], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vp + soff[t]),
-                                         (lds_ptr)&dst[1][(4 * wave + t) * 1024], 16, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+          // (the offset is taken here, so the loads address with scalar base + 32-bit offset)
+          unsigned o = soff[t];
+          asm volatile("" : "+v"(o));
+          __builtin_amdgcn_global_load_lds(kp + o, (lds_ptr)&dst[0][(4 * wave + t) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vp + o, (lds_ptr)&dst[1][(4 * wave + t) * 1024], 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool vin = sp * KPS * kSubTile + srw[t] < seq_len;
+          const char* kp = page >= 0 ? kbase + off : nan_rows;
+          const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
+          __builtin_amdgcn_global_load_lds((gptr)(kp + soff[t]), (lds_ptr)&dst[0][(4 * wave + t) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gptr)(vp + soff[t]), (lds_ptr)&dst[1][(4 * wave + t) * 1024], 16, 0, 0);
+        }
       }
     };
     auto steps = [&](int sp, char (&buf)[2][DMA ? DTILE : 16]) __attribute__((always_inline)) {
@@ -823,24 +849,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     // (s_waitcnt vmcnt(0) alone: the tile's HBM -> LDS transfers of this wave have landed)
     constexpr int kWaitVm0 = 0x0F70;
     const int nst = (nsub + KPS - 1) / KPS;
-    int pgn = pg_at(0);
-    dma(0, lds_d0, pgn);
-    pgn = pg_at(1);
+    dma(0, lds_d0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     // step sp from buffer sp % 2 while sp + 1 lands in the other (unrolled by two, so every
     // buffer access names its variable)
     for (int sp = 0; sp < nst; sp += 2) {
-      refill(4 * (sp + 2));
-      if (sp + 1 < nst) dma(sp + 1, lds_d1, pgn);
-      pgn = pg_at(sp + 2);
+      if (sp + 1 < nst) dma(sp + 1, lds_d1);
       steps(sp, lds_d0);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       if (sp + 1 >= nst) break;
-      refill(4 * (sp + 3));
-      if (sp + 2 < nst) dma(sp + 2, lds_d0, pgn);
-      pgn = pg_at(sp + 3);
+      if (sp + 2 < nst) dma(sp + 2, lds_d0);
       steps(sp + 1, lds_d1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
