@@ -317,15 +317,20 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
         if (key0 + F::vkey(i, g) >= u.seq_len) buf.v[i] = F::zero_v();
     }
     int posv[NB];
+    bool lov[NB];
+    const bool lo = needs_lo(pos);
 #pragma unroll
-    for (int cq = 0; cq < NB; ++cq) posv[cq] = pos;
+    for (int cq = 0; cq < NB; ++cq) {
+      posv[cq] = pos;
+      lov[cq] = lo;
+    }
     auto getK = [&](int kb, int s2) { return buf.k[kb][s2]; };
     auto getV = [&](int x) {
       if constexpr (std::is_same<E, float>::value) return buf.v[x];
       else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
     };
     subtile_step<E, D, NB>(st, qf, posv, getK, getV, a.cscale, key0, g, u.w0 + t == 0,
-                                  key0 + kSubTile - 1 > pos);
+                                  key0 + kSubTile - 1 > pos, lov, lo);
   };
   // Every sub-tile of unit u, its first one already in flight in b0. Even sub-tiles are
   // computed from b0 and odd ones from b1; the next unit's first sub-tile goes to b0, during
@@ -591,7 +596,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // (lc + 2 R) % 16): the same banks as a 32-byte row padding, which the K reads and the
   // transposing V reads use without conflicts.
   // Otherwise the sub-tile is staged through registers into one padded buffer.
-  constexpr bool DMA = BF && D == 128 && NW == 4 && NPF == 1;
+  constexpr bool DMA = BF && D == 128 && (NW == 4 || NW == 8) && NPF == 1;
   constexpr int KPS = 2;                                   // sub-tiles per DMA step
   constexpr int DTILE = KPS * kSubTile * LD::ROWB;         // 16 KB: 64 keys
   __shared__ __attribute__((aligned(16))) char lds_kv[2][DMA ? 16 : LD::TILE];
@@ -654,6 +659,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     for (int mb = 0; mb < NM; ++mb) Areg[AREG ? cb : 0][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // P_lo choice of the rows (their positions are fixed for the whole tile)
+  bool lo_c[NBW], lo_any_c = false;
+#pragma unroll
+  for (int cb = 0; cb < NBW; ++cb) {
+    lo_c[cb] = needs_lo(pos_c[cb]);
+    lo_any_c = lo_any_c || lo_c[cb];
+  }
+  const bool lo_w = wave_any(lo_any_c);
   const int nsub = bad_seq ? 0 : (pos_max_wg + kSubTile) / kSubTile;
   // page ids of the logical pages the tile reads, in an LDS ring of kPageCache entries
   // (logical page lp in slot lp % kPageCache), refilled half a ring ahead of use
@@ -735,11 +748,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     voff[x] = rv * LD::ROWB + (pchunk(2 * x + ((c & 3) >> 1), rv) << 4) + 8 * (c & 1);
   // one sub-tile step: compute sub-tile u from the K/V tile at kt / vt, then fold split j into
   // the row state when u ends it
+  // (sub-tiles come in ascending order: split j and the sub-tile's place in it are counted)
+  const int SS = S / kSubTile;
+  int sj = 0, sr = 0;
   auto step = [&](int u, const char* kt, const char* vt) __attribute__((always_inline)) {
     const int key0 = u * kSubTile;
-    const int j = key0 / S;
-    const bool first = key0 == j * S;
-    const bool last_of_split = key0 + kSubTile == (j + 1) * S || u + 1 == nsub;
+    const int j = sj;
+    const bool first = sr == 0;
+    const bool last_of_split = sr == SS - 1 || u + 1 == nsub;
+    if (++sr == SS) {
+      sr = 0;
+      ++sj;
+    }
     if (wave_max >= key0) {
       auto getK = [&](int kb, int s2) {
         if constexpr (DMA) return *(const u32x4*)(kt + koff[s2] + kb * 16 * LD::ROWB);
@@ -753,7 +773,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
       // all blocks advance together; on the diagonal of the tile the mask leaves rows whose
       // position is below key0 as they are (see subtile_step)
       subtile_step<E, D, NBW, BF>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
-                                  key0 + kSubTile - 1 > wave_min);
+                                  key0 + kSubTile - 1 > wave_min, lo_c, lo_w);
     }
     if (last_of_split && wave_max >= j * S) {
       // fold split j into the rows of every block that reaches it (also when this wave's rows
@@ -788,25 +808,27 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   };
 
   if constexpr (DMA) {
-    // A step covers KPS = 2 sub-tiles (64 keys, 4 pages). This wave's four 1 KB blocks of each
-    // step's tile: rows R = 16 wave + 4 t + lane / 16 (page `wave` of the step), lane's chunk at
-    // physical position lane % 16.
-    unsigned soff[4];
-    int srw[4];
+    // A step covers KPS = 2 sub-tiles (64 keys, 4 pages). This wave's TPW 1 KB blocks of each
+    // step's tile: rows R = RPW wave + 4 t + lane / 16, all in page PG of the step, lane's chunk
+    // at physical position lane % 16.
+    constexpr int RPW = KPS * kSubTile / NW, TPW = RPW / 4;
+    const int PG = RPW * wave / kPage;
+    unsigned soff[TPW];
+    int srw[TPW];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int R = 16 * wave + 4 * t + (lane >> 4), Rp = R & 15;
+    for (int t = 0; t < TPW; ++t) {
+      const int R = RPW * wave + 4 * t + (lane >> 4), Rp = R & 15;
       srw[t] = R;
       soff[t] = Rp * LD::ROWB + (((lane - 2 * Rp) & 15) << 4);   // logical chunk of physical lane % 16
     }
     // Page ids: lane i of pg_cur holds the page this wave reads in step pbase + i (logical page
-    // 4 (pbase + i) + wave, in sub-tile 2 (pbase + i) + wave / 2; -1 when that sub-tile is past
-    // the last one or the page must not be read), pg_nxt the next 64 steps' ids; a step takes
-    // its id with one readlane, so no memory wait sits between the steps' loads.
+    // 4 (pbase + i) + PG, in sub-tile 2 (pbase + i) + PG / 2; -1 when that sub-tile is past the
+    // last one or the page must not be read), pg_nxt the next 64 steps' ids; a step takes its id
+    // with one readlane, so no memory wait sits between the steps' loads.
     auto pg_batch = [&](int base) {
       const int sp = base + lane;
-      const int p = page_of_nb(a, b, 4 * sp + wave, seq_len);
-      return 2 * sp + (wave >> 1) <= last ? p : -1;
+      const int p = page_of_nb(a, b, 4 * sp + PG, seq_len);
+      return 2 * sp + (PG >> 1) <= last ? p : -1;
     };
     int pbase = 0;
     int pg_cur = pg_batch(0), pg_nxt = pg_batch(64);
@@ -820,25 +842,25 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
         pg_nxt = pg_batch(pbase + 64);
       }
       const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
-      if (page >= 0 && (4 * sp + wave + 1) * kPage <= seq_len) {
+      if (page >= 0 && (4 * sp + PG + 1) * kPage <= seq_len) {
         // the whole page lies before seq_len: one scalar base per page, lane offsets
         const gptr kp = (gptr)(kbase + off), vp = (gptr)(vbase + off);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < TPW; ++t) {
           // (the offset is taken here, so the loads address with scalar base + 32-bit offset)
           unsigned o = soff[t];
           asm volatile("" : "+v"(o));
-          __builtin_amdgcn_global_load_lds(kp + o, (lds_ptr)&dst[0][(4 * wave + t) * 1024], 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vp + o, (lds_ptr)&dst[1][(4 * wave + t) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(kp + o, (lds_ptr)&dst[0][(TPW * wave + t) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vp + o, (lds_ptr)&dst[1][(TPW * wave + t) * 1024], 16, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < TPW; ++t) {
           const bool vin = sp * KPS * kSubTile + srw[t] < seq_len;
           const char* kp = page >= 0 ? kbase + off : nan_rows;
           const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
-          __builtin_amdgcn_global_load_lds((gptr)(kp + soff[t]), (lds_ptr)&dst[0][(4 * wave + t) * 1024], 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((gptr)(vp + soff[t]), (lds_ptr)&dst[1][(4 * wave + t) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gptr)(kp + soff[t]), (lds_ptr)&dst[0][(TPW * wave + t) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gptr)(vp + soff[t]), (lds_ptr)&dst[1][(TPW * wave + t) * 1024], 16, 0, 0);
         }
       }
     };

@@ -375,6 +375,8 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 //   pos[b]        -> this lane's row position in block b
 //   first: first sub-tile of the split (state reset, not rescaled)
 //   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
+//   lo_row[b]: needs_lo(pos[b]); lo_any: some lane of the wave has lo_row (wave-uniform); both
+//          depend on the positions only, so callers compute them once
 //   A row with pos < key0 (all its keys masked) takes p = 0 everywhere, which leaves its state
 //   bitwise as it was; at a split start it gets the empty state (m = -inf, l = 0, acc = 0),
 //   which the ascending fold leaves bitwise unchanged (a = 1, b = 0).
@@ -384,7 +386,7 @@ template <typename E, int D, int NB, bool PIPE = false, class KGet, class VGet>
 __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Frag<E, D>::Q* q,
                                              const int* pos, KGet&& getK, VGet&& getV,
                                              float cscale, int key0, int g, bool first,
-                                             bool mask) {
+                                             bool mask, const bool (&lo_row)[NB], bool lo_any) {
   using F = Frag<E, D>;
   constexpr int NM = D / 16;
   typename F::Q qv[NB];
@@ -393,8 +395,6 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
   f32x4 s[NB][2];
   F::template qk<NB, PIPE>(s, getK, qv);
   float p[NB][2][4];
-  float mnew[NB], lnew[NB], alpha[NB];
-  bool need_any = false;
   float x[NB][2][4], mxl[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -416,28 +416,40 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
   // A row raises its reference only if some lane of it holds a scaled score above m + kLazy
   // (the scaled row max is the max of the lanes' scaled maxima: rounding is monotonic), so
   // the row max butterfly runs only at a split start or when some lane of the wave needs it.
-  bool any_up = first;
+  bool full = first;
   if (!first) {
+    unsigned long long up = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) any_up = any_up || (mxl[b] * cscale > st[b].m + kLazy);
+    for (int b = 0; b < NB; ++b) up |= __builtin_amdgcn_ballot_w64(mxl[b] * cscale > st[b].m + kLazy);
+    full = up != 0;
   }
-  const bool full = first || wave_any(any_up);
+  float mnew[NB], alpha[NB], lnew[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    bool need = false;
-    alpha[b] = first ? 0.f : 1.0f;
-    if (full) {
+    mnew[b] = st[b].m;
+    alpha[b] = 1.0f;
+  }
+  bool rescale = false;
+  if (full) {
+    unsigned long long need_any = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
       const float mt = xor_max(mxl[b]) * cscale;
       if (first) {
         mnew[b] = mt;
       } else {
-        need = mt > st[b].m + kLazy;
-        mnew[b] = need ? mt : st[b].m;
-        if (need) alpha[b] = ex2(st[b].m - mnew[b]);
+        const bool need = mt > st[b].m + kLazy;
+        if (need) {
+          mnew[b] = mt;
+          alpha[b] = ex2(st[b].m - mt);
+        }
+        need_any |= __builtin_amdgcn_ballot_w64(need);
       }
-    } else {
-      mnew[b] = st[b].m;
     }
+    rescale = !first && need_any != 0;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
     // (an all-masked row has mnew = -inf: the offset -FLT_MAX keeps its p = 2^-inf = 0)
     const float nm = -__builtin_fmaxf(mnew[b], -3.40282347e38f);
 #pragma unroll
@@ -447,22 +459,13 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
                      ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
     lnew[b] = first ? rs : __builtin_fmaf(st[b].l, alpha[b], rs);
-    need_any = need_any || need;
   }
-  bool lo_row[NB];
-  bool lo_any = false;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    lo_row[b] = needs_lo(pos[b]);
-    lo_any = lo_any || lo_row[b];
-  }
-  lo_any = wave_any(lo_any);
   if (first) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else if (wave_any(need_any)) {
+  } else if (rescale) {
     // alpha == 1 exactly for rows that kept their reference, so x * alpha == x
 #pragma unroll
     for (int b = 0; b < NB; ++b)
