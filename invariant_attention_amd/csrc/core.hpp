@@ -378,8 +378,8 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 //   lo_row[b]: needs_lo(pos[b]); lo_any: some lane of the wave has lo_row (wave-uniform); both
 //          depend on the positions only, so callers compute them once
 //   A row with pos < key0 (all its keys masked) takes p = 0 everywhere, which leaves its state
-//   bitwise as it was; at a split start it gets the empty state (m = -inf, l = 0, acc = 0),
-//   which the ascending fold leaves bitwise unchanged (a = 1, b = 0).
+//   bitwise as it was; at a split start it gets the empty state (m = -FLT_MAX, l = 0,
+//   acc = 0), which the ascending fold leaves bitwise unchanged (a = 1, b = 0).
 //   PIPE:  operand reads are issued ahead of the MFMAs that use them (LDS operands): K one
 //          k-step ahead, V two row blocks ahead
 template <typename E, int D, int NB, bool PIPE = false, class KGet, class VGet>
@@ -436,7 +436,9 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     for (int b = 0; b < NB; ++b) {
       const float mt = xor_max(mxl[b]) * cscale;
       if (first) {
-        mnew[b] = mt;
+        // an all-masked row (a prefill row below the split's first key) takes the reference
+        // -FLT_MAX, so its p = 2^-inf = 0 with a finite offset
+        mnew[b] = mt > -3.40282347e38f ? mt : -3.40282347e38f;
       } else {
         const bool need = mt > st[b].m + kLazy;
         if (need) {
@@ -450,8 +452,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    // (an all-masked row has mnew = -inf: the offset -FLT_MAX keeps its p = 2^-inf = 0)
-    const float nm = -__builtin_fmaxf(mnew[b], -3.40282347e38f);
+    const float nm = -mnew[b];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -492,8 +493,8 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 // L = l b + L a, A = acc b + A a, each one fma with the rounded product of the row state as
 // addend (so A can be updated in place). The row state starts at (M, L, A) = (-inf, 0, 0), so
 // split 0 gives a = 0, b = 1 and copies its state exactly (x 1 + 0 = x for the never
-// negative-zero partials) with no special case; an empty split (m = -inf, l = 0, acc = 0)
-// gives a = 1, b = 0 and leaves the row state as it was.
+// negative-zero partials) with no special case; an empty split (m = -FLT_MAX, l = 0,
+// acc = 0) gives a = 1, b = 0 and leaves a row state with finite M as it was.
 __device__ __forceinline__ void fold_scalars(float& M, float& L, float m, float l, float& a, float& b) {
   const float Mn = fmaxf(M, m);
   a = ex2(M - Mn);
