@@ -957,6 +957,11 @@ __global__ __launch_bounds__(256) void page_update_kernel(const char* k_new, con
   const int lane = threadIdx.x & 63;
   const int t0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int first = q_starts[0], end = q_starts[batch];
+  // up to 64 sequences: every lane holds q_starts[lane] and seq_lens[lane], loaded with the
+  // token rows, so the page id is one load after them
+  const bool small = batch <= 64;
+  const int qs_l = small && lane <= batch ? q_starts[lane] : 0;
+  const int sl_l = small && lane < batch ? seq_lens[lane] : 0;
   for (int t = t0; t < total_tokens; t += (int)gridDim.x * 4) {
     if (t < first || t >= end) continue;
     // the token's first 64 chunks are loaded before its page is known
@@ -965,15 +970,25 @@ __global__ __launch_bounds__(256) void page_update_kernel(const char* k_new, con
     const size_t src0 = ((size_t)t * hkv + (l0 ? h0 : 0)) * ROWB + (l0 ? ch0 : 0) * 16;
     const u32x4 k0 = *(const u32x4*)(k_new + src0);
     const u32x4 v0 = *(const u32x4*)(v_new + src0);
-    int cnt = 0;
-    for (int c0 = 0; c0 < batch; c0 += 64) {
-      const int i = c0 + lane;
-      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < batch && q_starts[i] <= t));
+    int bq, s0, s1, len;                            // bq: last b with q_starts[b] <= t
+    if (small) {
+      bq = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < batch && qs_l <= t)) - 1;
+      s0 = __builtin_amdgcn_readlane(qs_l, bq);
+      s1 = bq + 1 < 64 ? __builtin_amdgcn_readlane(qs_l, bq + 1) : end;
+      len = __builtin_amdgcn_readlane(sl_l, bq);
+    } else {
+      int cnt = 0;
+      for (int c0 = 0; c0 < batch; c0 += 64) {
+        const int i = c0 + lane;
+        cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < batch && q_starts[i] <= t));
+      }
+      bq = cnt - 1;
+      s0 = q_starts[bq];
+      s1 = q_starts[bq + 1];
+      len = seq_lens[bq];
     }
-    const int bq = cnt - 1;                         // last b with q_starts[b] <= t
-    const int s0 = q_starts[bq], s1 = q_starts[bq + 1];
     if (t >= s1) continue;                          // q_starts not ascending: not a token of bq
-    const int pos = seq_lens[bq] - (s1 - s0) + (t - s0);
+    const int pos = len - (s1 - s0) + (t - s0);
     if (pos < 0) continue;
     const int lp = pos / kPage;
     if (lp >= max_pages) continue;
