@@ -156,6 +156,25 @@ int bi_attn_prefill(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
                     int32_t batch, int32_t total_tokens, int32_t max_q_len, int32_t max_seq_len,
                     float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Dense varlen attention, the trainer-side form of chunked prefill: K and V are contiguous
+ * arrays [total_k][Hkv][D] (not a paged cache), sequence b owning rows k_starts[b] ..
+ * k_starts[b+1] - 1 (k_starts ascending, k_starts[batch] <= total_k), so seq_len[b] =
+ * k_starts[b+1] - k_starts[b]. Its n_new[b] = q_starts[b+1] - q_starts[b] queries (rows of q
+ * [total_q][Hq][D]) are its last n_new positions, causal as in bi_attn_prefill. Sampling and
+ * training must agree bit for bit for on-policy reinforcement learning (xitu-tech.com report,
+ * section 强化学习的突破; neican.ai insight page, section 未来发展路径预测, true on-policy RL
+ * item): this call runs the prefill kernel's arithmetic on the dense layout, so each output
+ * row is bit-identical to bi_attn_prefill / bi_attn_decode on the same keys and values held
+ * in a paged cache (any page placement, any batch, any chunking), within one build on one
+ * device. A sequence whose k_starts entries are out of range, or with n_new > seq_len or
+ * seq_len > max_seq_len, gets NaN rows. max_q_len >= every n_new[b]. No workspace.
+ */
+int bi_attn_varlen(const bi_attn_cfg* cfg, const void* q, const void* k, const void* v,
+                   const int32_t* q_starts, const int32_t* k_starts, int32_t batch,
+                   int32_t total_q, int32_t total_k, int32_t max_q_len, int32_t max_seq_len,
+                   float* out, hipStream_t stream);
+
 /* Static English text for a bi_status value (never NULL). */
 const char* bi_status_string(int status);
 

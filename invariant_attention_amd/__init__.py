@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     bi_attn_decode_combine,
     bi_attn_decode_partials,
     bi_attn_prefill,
+    bi_attn_varlen,
     bi_attn_workspace_bytes,
     bi_kv_page_update,
     bi_status_string,

@@ -24,7 +24,7 @@ BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode",
             "bi_attn_decode_partials", "bi_attn_decode_combine", "bi_attn_prefill",
-            "bi_status_string")
+            "bi_attn_varlen", "bi_status_string")
 
 
 class BiAttnError(RuntimeError):
@@ -90,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.bi_attn_decode_combine.argtypes = [CP, P, I, I, P, P, Z, P]
     lib.bi_attn_prefill.restype = ctypes.c_int
     lib.bi_attn_prefill.argtypes = [CP, P, P, P, P, I, I, P, P, I, I, I, I, P, P, Z, P]
+    lib.bi_attn_varlen.restype = ctypes.c_int
+    lib.bi_attn_varlen.argtypes = [CP, P, P, P, P, P, I, I, I, I, I, P, P]
     _lib = lib
     return lib
 
@@ -177,3 +179,15 @@ def bi_attn_prefill(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_c
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "bi_attn_prefill")
+
+
+def bi_attn_varlen(cfg: AttnConfig, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   q_starts: torch.Tensor, k_starts: torch.Tensor, max_q_len: int,
+                   max_seq_len: int, out: torch.Tensor, stream=None) -> None:
+    """Dense varlen attention: ``k``, ``v`` ``[total_k][Hkv][D]``, sequence ``b`` owning rows
+    ``k_starts[b] .. k_starts[b+1]-1``; ``q [T][Hq][D]``; ``out`` fp32 ``[T][Hq][D]``."""
+    st = load().bi_attn_varlen(
+        ctypes.byref(cfg.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(q_starts), _ptr(k_starts),
+        k_starts.shape[0] - 1, q.shape[0], k.shape[0], int(max_q_len), int(max_seq_len),
+        _ptr(out), _stream(stream))
+    _check(st, "bi_attn_varlen")

@@ -31,10 +31,12 @@ struct AttnParams {
   const int32_t* page_table;
   const int32_t* seq_lens;
   const int32_t* q_starts;   // prefill only
+  const int32_t* k_starts;   // dense (varlen) prefill only: first K/V row of each sequence
   float* out;
   float* ws_acc;             // decode: [batch Hkv][jmax][group][D]
   float2* ws_ml;             // decode: [batch Hkv][jmax][group]  (m, l)
   int32_t max_pages, num_pages, batch, total_tokens, max_q_len, max_seq_len;
+  int32_t k_rows;            // dense: rows of the K and V arrays
   int32_t hq, hkv, group, split, policy, num_cus, jmax;
   float cscale;              // softmax scale * log2(e)
 };
@@ -523,10 +525,18 @@ __device__ __forceinline__ PfSeq pf_seq(const AttnParams& a, int b, int tq) {
   if (b >= a.batch) return s;
   const int q0 = a.q_starts[b], q1 = a.q_starts[b + 1];
   if (q1 > a.total_tokens || q0 < 0 || q1 <= q0) return s;
-  const int len = a.seq_lens[b];
+  int len;
+  bool rows_ok = true;
+  if (a.k_starts) {
+    const int k0 = a.k_starts[b], k1 = a.k_starts[b + 1];
+    len = k1 - k0;
+    rows_ok = k0 >= 0 && k1 <= a.k_rows;
+  } else {
+    len = a.seq_lens[b];
+  }
   s.n = q1 - q0;
   s.nt = (s.n + tq - 1) / tq;
-  s.bad = len > a.max_seq_len || s.n > len;
+  s.bad = len > a.max_seq_len || s.n > len || !rows_ok;
   s.fp = len - s.n;
   return s;
 }
@@ -579,7 +589,7 @@ __device__ bool pf_item(const AttnParams& a, int tq, int i, int& ob, int& otile)
   return false;
 }
 
-template <typename E, int D, int NBW, int NW, bool RING, int NPF, bool AREG, int MINB>
+template <typename E, int D, int NBW, int NW, bool RING, int NPF, bool AREG, int MINB, bool DENSE>
 __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   using F = Frag<E, D>;
   using LD = Lds<D, E>;
@@ -618,14 +628,22 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   const int q0 = a.q_starts[b], q1 = a.q_starts[b + 1];
   const int n_new = q1 - q0;
   const int t0 = tile * tq;
-  const int seq_len = a.seq_lens[b];
-  const bool bad_seq = seq_len > a.max_seq_len || n_new > seq_len;
+  // dense: the sequence's keys are rows k0 .. k0 + seq_len - 1 of [k_rows][Hkv][D] arrays
+  const int k0 = DENSE ? a.k_starts[b] : 0;
+  const int seq_len = DENSE ? a.k_starts[b + 1] - k0 : a.seq_lens[b];
+  const bool bad_seq = seq_len > a.max_seq_len || n_new > seq_len || (DENSE && (k0 < 0 || k0 + seq_len > a.k_rows));
   const int first_pos = seq_len - n_new;
   const int t_last = min(t0 + tq, n_new) - 1;
   const int pos_max_wg = first_pos + t_last;
   const int S = split_len(a, seq_len);
   const size_t head_stride = (size_t)kPage * LD::ROWB;
   const size_t page_stride = (size_t)a.hkv * head_stride;
+  // bytes between consecutive keys of one KV head in HBM (paged: rows of a page; dense: rows of
+  // the [k_rows][Hkv][D] arrays), and the offset of logical page lp (16 keys) from the head base
+  const int rstride = DENSE ? a.hkv * LD::ROWB : LD::ROWB;
+  auto page_off = [&](int page) -> size_t {
+    return DENSE ? (size_t)(k0 + kPage * page) * (size_t)rstride : (size_t)(unsigned)max(page, 0) * page_stride;
+  };
 
   typename F::Q qf[NBW];
   RowState<D> st[NBW];
@@ -671,14 +689,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // page ids of the logical pages the tile reads, in an LDS ring of kPageCache entries
   // (logical page lp in slot lp % kPageCache), refilled half a ring ahead of use
   const int npg_total = nsub * (kSubTile / kPage);
-  if constexpr (!DMA) {
+  if constexpr (!DMA && !DENSE) {
     for (int i = threadIdx.x; i < min(npg_total, kPageCache); i += NT) lds_pages[i] = page_of(a, b, i, seq_len);
     __syncthreads();
   }
 
   // staging: each thread owns the same (row, 16-byte chunk) slots of the K and V sub-tiles
-  const char* kbase = a.k_cache + kvh * head_stride;
-  const char* vbase = a.v_cache + kvh * head_stride;
+  const char* kbase = a.k_cache + kvh * (DENSE ? (size_t)LD::ROWB : head_stride);
+  const char* vbase = a.v_cache + kvh * (DENSE ? (size_t)LD::ROWB : head_stride);
   // A ring of NPF register sets keeps NPF sub-tiles of loads in flight. The loop is unrolled
   // by NPF so every set has a fixed name, and every stage issues exactly the same loads, so
   // the wait before each LDS store counts exactly the later loads. Absent pages and sub-tiles
@@ -706,7 +724,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   auto page_at = [&](int u, int k) {
     const unsigned half = UNI ? (unsigned)(k * NT / (kPage * CHUNKS)) : srow[k] / kPage;
     const unsigned lp = 2u * (unsigned)u + half;
-    return u <= last ? lds_pages[lp % kPageCache] : -1;
+    if constexpr (DENSE) return u <= last && (int)lp * kPage < seq_len ? (int)lp : -1;
+    else return u <= last ? lds_pages[lp % kPageCache] : -1;
   };
   int pgq[PP];
   auto stage_load = [&](int u, const int (&pgs)[PP], u32x4 (&pk)[PP], u32x4 (&pv)[PP]) {
@@ -715,11 +734,19 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
       int page = pgs[k];
       if (UNI) page = __builtin_amdgcn_readfirstlane(page);
       const bool vin = u * kSubTile + (int)srow[k] < seq_len;
-      const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
-      const char* kp = page >= 0 ? kbase + off : nan_rows;
-      const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
-      pk[k] = *(const u32x4*)(kp + sin_page[k]);
-      pv[k] = *(const u32x4*)(vp + sin_page[k]);
+      if constexpr (DENSE) {
+        // rows at or past seq_len are another sequence's (or past the arrays): stand-ins
+        const bool in = page >= 0 && vin;
+        const size_t off = page_off(page) + (size_t)(srow[k] % kPage) * (unsigned)(rstride - LD::ROWB);
+        pk[k] = *(const u32x4*)((in ? kbase + off : nan_rows) + sin_page[k]);
+        pv[k] = *(const u32x4*)((in ? vbase + off : zero_rows) + sin_page[k]);
+      } else {
+        const size_t off = page_off(page);
+        const char* kp = page >= 0 ? kbase + off : nan_rows;
+        const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
+        pk[k] = *(const u32x4*)(kp + sin_page[k]);
+        pv[k] = *(const u32x4*)(vp + sin_page[k]);
+      }
     }
   };
   auto stage_store = [&](const u32x4 (&pk)[PP], const u32x4 (&pv)[PP]) {
@@ -800,7 +827,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   // it; the slots it overwrites belong to pages no later read needs, and the end-of-step
   // barriers order the refill against the earlier readers and the later ones
   auto refill = [&](int lpn) {
-    if (RING && lpn % (kPageCache / 2) == 0 && lpn >= kPageCache / 2) {
+    if (RING && !DENSE && lpn % (kPageCache / 2) == 0 && lpn >= kPageCache / 2) {
       const int base = lpn + kPageCache / 2;
       for (int t = threadIdx.x; t < kPageCache / 2; t += NT)
         if (base + t < npg_total) lds_pages[(base + t) % kPageCache] = page_of(a, b, base + t, seq_len);
@@ -819,13 +846,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     for (int t = 0; t < TPW; ++t) {
       const int R = RPW * wave + 4 * t + (lane >> 4), Rp = R & 15;
       srw[t] = R;
-      soff[t] = Rp * LD::ROWB + (((lane - 2 * Rp) & 15) << 4);   // logical chunk of physical lane % 16
+      soff[t] = Rp * rstride + (((lane - 2 * Rp) & 15) << 4);   // logical chunk of physical lane % 16
     }
     // Page ids: lane i of pg_cur holds the page this wave reads in step pbase + i (logical page
     // 4 (pbase + i) + PG, in sub-tile 2 (pbase + i) + PG / 2; -1 when that sub-tile is past the
     // last one or the page must not be read), pg_nxt the next 64 steps' ids; a step takes its id
     // with one readlane, so no memory wait sits between the steps' loads.
     auto pg_batch = [&](int base) {
+      if constexpr (DENSE) return 0;
       const int sp = base + lane;
       const int p = page_of_nb(a, b, 4 * sp + PG, seq_len);
       return 2 * sp + (PG >> 1) <= last ? p : -1;
@@ -835,13 +863,20 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     typedef __attribute__((address_space(3))) void* lds_ptr;
     typedef const __attribute__((address_space(1))) char* gptr;
     auto dma = [&](int sp, char (&dst)[2][DMA ? DTILE : 16]) __attribute__((always_inline)) {
-      const int page = __builtin_amdgcn_readlane(pg_cur, sp - pbase);
-      if (sp - pbase == 63) {
-        pbase += 64;
-        pg_cur = pg_nxt;
-        pg_nxt = pg_batch(pbase + 64);
+      int page;
+      if constexpr (DENSE) {
+        // no table: logical page 4 sp + PG, absent past the last sub-tile or the sequence end
+        const int lp = 4 * sp + PG;
+        page = 2 * sp + (PG >> 1) <= last && lp * kPage < seq_len ? lp : -1;
+      } else {
+        page = __builtin_amdgcn_readlane(pg_cur, sp - pbase);
+        if (sp - pbase == 63) {
+          pbase += 64;
+          pg_cur = pg_nxt;
+          pg_nxt = pg_batch(pbase + 64);
+        }
       }
-      const size_t off = (size_t)(unsigned)max(page, 0) * page_stride;
+      const size_t off = page_off(page);
       if (page >= 0 && (4 * sp + PG + 1) * kPage <= seq_len) {
         // the whole page lies before seq_len: one scalar base per page, lane offsets
         const gptr kp = (gptr)(kbase + off), vp = (gptr)(vbase + off);
@@ -857,10 +892,20 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           const bool vin = sp * KPS * kSubTile + srw[t] < seq_len;
-          const char* kp = page >= 0 ? kbase + off : nan_rows;
-          const char* vp = page >= 0 && vin ? vbase + off : zero_rows;
-          __builtin_amdgcn_global_load_lds((gptr)(kp + soff[t]), (lds_ptr)&dst[0][(TPW * wave + t) * 1024], 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((gptr)(vp + soff[t]), (lds_ptr)&dst[1][(TPW * wave + t) * 1024], 16, 0, 0);
+          const char *kp, *vp;
+          if constexpr (DENSE) {
+            // rows at or past seq_len belong to another sequence (or lie past the arrays): both
+            // K and V read stand-ins there, at the stand-ins' own row pitch
+            const bool in = page >= 0 && vin;
+            const unsigned std_off = soff[t] - (unsigned)(srw[t] & 15) * (unsigned)(rstride - LD::ROWB);
+            kp = in ? kbase + off + soff[t] : nan_rows + std_off;
+            vp = in ? vbase + off + soff[t] : zero_rows + std_off;
+          } else {
+            kp = (page >= 0 ? kbase + off : nan_rows) + soff[t];
+            vp = (page >= 0 && vin ? vbase + off : zero_rows) + soff[t];
+          }
+          __builtin_amdgcn_global_load_lds((gptr)kp, (lds_ptr)&dst[0][(TPW * wave + t) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gptr)vp, (lds_ptr)&dst[1][(TPW * wave + t) * 1024], 16, 0, 0);
         }
       }
     };
@@ -1181,20 +1226,20 @@ int dispatch_partials(const bi_attn_cfg* cfg, const AttnParams& a, hipStream_t s
 // bf16: two workgroups of 4 waves per CU (their barriers are independent, so one fills the
 // other's stalls), 2 column blocks per wave, A in registers, one staging set in flight (the
 // other workgroup's loads cover the latency). fp32: one workgroup of 4 waves, A in LDS.
-template <typename E, int D>
+template <typename E, int D, bool DENSE = false>
 int launch_prefill(const AttnParams& a, hipStream_t s) {
   constexpr bool BF = std::is_same<E, __bf16>::value;
   constexpr int NW = 4, NBW = 2, NPF = BF ? 1 : 4, MINB = BF ? 2 : 1;
   constexpr bool AREG = BF;
-  // sequences longer than the LDS page-id ring need the kernel that refills it
-  const bool ring = (int64_t)a.max_seq_len + kSubTile > (int64_t)kPageCache * kPage;
+  // sequences longer than the LDS page-id ring need the kernel that refills it (paged layout)
+  const bool ring = !DENSE && (int64_t)a.max_seq_len + kSubTile > (int64_t)kPageCache * kPage;
   const int tq = NW * NBW * 16 / a.group;
   // one workgroup per (tile, KV head); workgroups past the real item count exit at once
   const int64_t wgs = (int64_t)((a.max_q_len + tq - 1) / tq) * a.batch * a.hkv;
   if (wgs > 0x7fffffff) return BI_EUNSUPPORTED;
   const dim3 grid((unsigned)wgs);
-  if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, true, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
-  else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, NPF, AREG, MINB>), grid, dim3(64 * NW), 0, s, a);
+  if (ring) hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, true, NPF, AREG, MINB, false>), grid, dim3(64 * NW), 0, s, a);
+  else hipLaunchKernelGGL((prefill_kernel<E, D, NBW, NW, false, NPF, AREG, MINB, DENSE>), grid, dim3(64 * NW), 0, s, a);
   return launched();
 }
 
@@ -1311,6 +1356,35 @@ int bi_attn_prefill(const bi_attn_cfg* cfg, const void* q, const void* k_cache, 
   const bool bf = cfg->dtype == BI_BF16;
   if (cfg->head_dim == 128) return bf ? launch_prefill<__bf16, 128>(a, stream) : launch_prefill<float, 128>(a, stream);
   return bf ? launch_prefill<__bf16, 64>(a, stream) : launch_prefill<float, 64>(a, stream);
+}
+
+int bi_attn_varlen(const bi_attn_cfg* cfg, const void* q, const void* k, const void* v,
+                   const int32_t* q_starts, const int32_t* k_starts, int32_t batch, int32_t total_q,
+                   int32_t total_k, int32_t max_q_len, int32_t max_seq_len, float* out,
+                   hipStream_t stream) {
+  int st = check_cfg(cfg);
+  if (st != BI_OK) return st;
+  if (batch < 0 || total_q < 0 || total_k < 0 || max_q_len < 0 || max_seq_len < 0) return BI_EINVAL;
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return BI_OK;
+  if (!q || !k || !v || !q_starts || !k_starts || !out) return BI_EINVAL;
+  if (max_seq_len == 0 || total_k == 0) return BI_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BI_EINVAL;
+  AttnParams a = base_params(cfg);
+  a.q = (const char*)q;
+  a.k_cache = (const char*)k;
+  a.v_cache = (const char*)v;
+  a.q_starts = q_starts;
+  a.k_starts = k_starts;
+  a.k_rows = total_k;
+  a.out = out;
+  a.batch = batch;
+  a.total_tokens = total_q;
+  a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  const bool bf = cfg->dtype == BI_BF16;
+  if (cfg->head_dim == 128)
+    return bf ? launch_prefill<__bf16, 128, true>(a, stream) : launch_prefill<float, 128, true>(a, stream);
+  return bf ? launch_prefill<__bf16, 64, true>(a, stream) : launch_prefill<float, 64, true>(a, stream);
 }
 
 }  // extern "C"

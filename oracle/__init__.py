@@ -5,6 +5,7 @@ from .attention import (  # noqa: F401
     gather_kv,
     paged_attention,
     paged_attention_rows,
+    varlen_attention,
     split_bounds,
     split_partial,
     fold,

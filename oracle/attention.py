@@ -84,7 +84,6 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     definition (one matrix product for the scores, one for the output).
     """
     T, Hq, D = q.shape
-    G = Hq // num_kv_heads
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     out = np.empty((T, Hq, D), np.float64)
     for b in range(len(seq_lens)):
@@ -92,21 +91,54 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         if r1 == r0:
             continue
         L = int(seq_lens[b])
-        first = L - (r1 - r0)
         K = gather_kv(k_cache, page_table[b], L)
         V = gather_kv(v_cache, page_table[b], L)
-        for t0 in range(r0, r1, row_block):
-            t1 = min(t0 + row_block, r1)
-            pos = first + np.arange(t0 - r0, t1 - r0)            # absolute positions
-            nk = int(pos[-1]) + 1                                 # keys any row may see
-            masked = np.arange(nk)[None, :] > pos[:, None]        # [rows][keys]
-            mask_rows = np.repeat(masked, G, axis=0)                # row = token * G + head
-            for g in range(num_kv_heads):
-                Qg = q[t0:t1, g * G:(g + 1) * G, :].astype(np.float64).reshape(-1, D)
-                S = (Qg @ K[:nk, g, :].T) * sc
-                S[mask_rows] = -np.inf
-                W = _softmax_rows(S)
-                out[t0:t1, g * G:(g + 1) * G, :] = (W @ V[:nk, g, :]).reshape(t1 - t0, G, D)
+        _causal_rows(q, K, V, r0, r1, num_kv_heads, sc, row_block, out)
+    return out
+
+
+def _causal_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, r0: int, r1: int,
+                 num_kv_heads: int, sc: float, row_block: int, out: np.ndarray) -> None:
+    """Rows ``r0 .. r1-1`` of ``q`` are the last ``r1 - r0`` positions of one sequence whose
+    keys and values are ``K``, ``V`` ``[L][Hkv][D]`` float64; writes their outputs."""
+    D = q.shape[2]
+    G = q.shape[1] // num_kv_heads
+    first = K.shape[0] - (r1 - r0)
+    for t0 in range(r0, r1, row_block):
+        t1 = min(t0 + row_block, r1)
+        pos = first + np.arange(t0 - r0, t1 - r0)            # absolute positions
+        nk = int(pos[-1]) + 1                                 # keys any row may see
+        masked = np.arange(nk)[None, :] > pos[:, None]        # [rows][keys]
+        mask_rows = np.repeat(masked, G, axis=0)                # row = token * G + head
+        for g in range(num_kv_heads):
+            Qg = q[t0:t1, g * G:(g + 1) * G, :].astype(np.float64).reshape(-1, D)
+            S = (Qg @ K[:nk, g, :].T) * sc
+            S[mask_rows] = -np.inf
+            W = _softmax_rows(S)
+            out[t0:t1, g * G:(g + 1) * G, :] = (W @ V[:nk, g, :]).reshape(t1 - t0, G, D)
+
+
+def varlen_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_starts: np.ndarray,
+                     k_starts: np.ndarray, num_kv_heads: int, scale: Optional[float] = None,
+                     row_block: int = 64) -> np.ndarray:
+    """The same causal GQA attention with dense keys: ``k``, ``v`` ``[total_k][Hkv][D]``,
+    sequence ``b`` owning rows ``k_starts[b] .. k_starts[b+1]-1``, its queries being its last
+    ``q_starts[b+1] - q_starts[b]`` positions. float64 ``[T][Hq][D]``.
+
+    A trainer computes this form; the sampler computes the paged one, and on-policy training
+    needs the two to agree (xitu-tech.com report, section 强化学习的突破). Mathematically it is
+    ``paged_attention`` with the sequence's pages laid end to end.
+    """
+    T, Hq, D = q.shape
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = np.empty((T, Hq, D), np.float64)
+    for b in range(len(k_starts) - 1):
+        r0, r1 = int(q_starts[b]), int(q_starts[b + 1])
+        if r1 == r0:
+            continue
+        k0, k1 = int(k_starts[b]), int(k_starts[b + 1])
+        _causal_rows(q, k[k0:k1].astype(np.float64), v[k0:k1].astype(np.float64), r0, r1,
+                     num_kv_heads, sc, row_block, out)
     return out
 
 

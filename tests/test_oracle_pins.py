@@ -126,6 +126,35 @@ def test_torch_sdpa_float64():
         t += n
 
 
+@pytest.mark.parametrize("seed", [0, 3])
+def test_varlen_brute_force_tiny(seed):
+    """The dense (varlen) form against the pure-Python definition, sequences laid end to end."""
+    c = random_case(seed, lens=(7, 20, 1, 33), n_new=(7, 4, 1, 9))
+    k = np.concatenate(c["ks"]); v = np.concatenate(c["vs"])
+    k_starts = np.concatenate([[0], np.cumsum([x.shape[0] for x in c["ks"]])]).astype(np.int32)
+    got = oracle.varlen_attention(c["q"], k, v, c["q_starts"], k_starts, c["Hkv"])
+    ref = brute_force(c["q"], c["ks"], c["vs"], c["n_new"])
+    np.testing.assert_allclose(got, ref, atol=1e-12, rtol=0)
+
+
+def test_varlen_torch_sdpa_float64():
+    c = random_case(12, Hq=8, Hkv=2, D=16, lens=(50, 16, 3), n_new=(50, 5, 1), page_size=16)
+    k = np.concatenate(c["ks"]); v = np.concatenate(c["vs"])
+    k_starts = np.array([0, 50, 66, 69], np.int32)
+    got = oracle.varlen_attention(c["q"], k, v, c["q_starts"], k_starts, 2)
+    G, t = 4, 0
+    for b, kb_np in enumerate(c["ks"]):
+        L, n = kb_np.shape[0], c["n_new"][b]
+        pos = torch.arange(L - n, L)
+        mask = torch.arange(L)[None, :] <= pos[:, None]
+        qb = torch.from_numpy(c["q"][t:t + n]).permute(1, 0, 2)
+        kb = torch.from_numpy(np.repeat(kb_np, G, axis=1)).permute(1, 0, 2)
+        vb = torch.from_numpy(np.repeat(c["vs"][b], G, axis=1)).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask)
+        np.testing.assert_allclose(got[t:t + n], ref.permute(1, 0, 2).numpy(), atol=1e-12, rtol=0)
+        t += n
+
+
 # ----------------------------------------------------------------------------- invariants
 def test_weights_sum_to_one():
     c = random_case(3)
