@@ -323,7 +323,45 @@ def run_prefill_bench(args, result):
                                   "traffic": profiled_traffic("prefill_kernel")}
     result["variant_slowdown"]["prefill"] = kern / kern_v - 1.0 if kern_v else None
     result["variant_slowdown"]["prefill_ms"] = {"invariant": kern, "split_by_batch": kern_v}
+    if not args.profile_run:
+        run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref)
     return bt, ref
+
+
+def run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref):
+    """The same prefill workload through bi_attn_varlen (dense [rows][Hkv][D] keys and values,
+    the trainer's layout): bits against the paged prefill, and kernel time."""
+    ks, vs = [], []
+    for b in range(bt.batch):
+        L = int(bt.seq_lens[b])
+        npg = (L + 15) // 16
+        pages = pt[b, :npg].long()
+        for cache, dst in ((kc, ks), (vc, vs)):
+            blk = cache[pages]
+            dst.append(blk.permute(0, 2, 1, 3).reshape(npg * 16, shape.num_kv_heads, shape.head_dim)[:L])
+    kd, vd = torch.cat(ks).contiguous(), torch.cat(vs).contiguous()
+    k_starts = dev(np.concatenate([[0], np.cumsum(bt.seq_lens)]).astype(np.int32), torch.int32)
+    qs = dev(bt.q_starts, torch.int32)
+    out = torch.empty_like(ref)
+    bi.bi_attn_varlen(cfg, q, kd, vd, qs, k_starts, bt.max_q_len, bt.max_seq_len, out)
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), "varlen vs paged prefill bits"
+    n = max(3, args.steps // 5)
+    for _ in range(2):
+        bi.bi_attn_varlen(cfg, q, kd, vd, qs, k_starts, bt.max_q_len, bt.max_seq_len, out)
+    tm = Timer(2)
+    torch.cuda.synchronize()
+    tm.mark(0)
+    for _ in range(n):
+        bi.bi_attn_varlen(cfg, q, kd, vd, qs, k_starts, bt.max_q_len, bt.max_seq_len, out)
+    tm.mark(1)
+    torch.cuda.synchronize()
+    ms = tm.ms(0, 1) / n
+    result["varlen"] = {"kernel_tflops": prefill_flops(bt) / (ms * 1e-3) / 1e12, "kernel_ms": ms,
+                        "unit": "TFLOP/s",
+                        "bits": "all rows equal to the paged prefill of the same keys and values",
+                        "config": {"workload": "the prefill workload with dense keys and values "
+                                               "[rows][Hkv][D] (bi_attn_varlen)"}}
+    log(f"varlen (dense K/V): {result['varlen']['kernel_tflops']:.1f} TFLOP/s, same bits as paged")
 
 
 # ----------------------------------------------------------------------------- CPU baseline
