@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     bi_attn_varlen,
     bi_attn_workspace_bytes,
     bi_kv_page_update,
+    bi_rmsnorm,
     bi_status_string,
     load,
 )

@@ -24,7 +24,7 @@ BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode",
             "bi_attn_decode_partials", "bi_attn_decode_combine", "bi_attn_prefill",
-            "bi_attn_varlen", "bi_status_string")
+            "bi_attn_varlen", "bi_status_string", "bi_rmsnorm")
 
 
 class BiAttnError(RuntimeError):
@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
     lib.bi_attn_prefill.restype = ctypes.c_int
     lib.bi_attn_prefill.argtypes = [CP, P, P, P, P, I, I, P, P, I, I, I, I, P, P, Z, P]
     lib.bi_attn_varlen.restype = ctypes.c_int
+    lib.bi_rmsnorm.restype = ctypes.c_int
+    lib.bi_rmsnorm.argtypes = [P, P, P, I, I, I, ctypes.c_float, P]
     lib.bi_attn_varlen.argtypes = [CP, P, P, P, P, P, I, I, I, I, I, P, P]
     _lib = lib
     return lib
@@ -191,3 +193,15 @@ def bi_attn_varlen(cfg: AttnConfig, q: torch.Tensor, k: torch.Tensor, v: torch.T
         k_starts.shape[0] - 1, q.shape[0], k.shape[0], int(max_q_len), int(max_seq_len),
         _ptr(out), _stream(stream))
     _check(st, "bi_attn_varlen")
+
+
+def bi_rmsnorm(x: torch.Tensor, weight: torch.Tensor, y: torch.Tensor, eps: float,
+               stream=None) -> None:
+    """Batch-invariant RMSNorm of ``x [rows][hidden]`` (bf16 or fp32) into ``y`` (same shape
+    and dtype) with ``weight [hidden]``; one wavefront reduces each row."""
+    if x.dtype not in (torch.bfloat16, torch.float32) or y.dtype != x.dtype or weight.dtype != x.dtype:
+        raise BiAttnError(BI_EINVAL, "bi_rmsnorm")
+    st = load().bi_rmsnorm(_ptr(x), _ptr(weight), _ptr(y), x.shape[0], x.shape[1],
+                           BI_BF16 if x.dtype == torch.bfloat16 else BI_F32, float(eps),
+                           _stream(stream))
+    _check(st, "bi_rmsnorm")

@@ -1,4 +1,5 @@
-"""Build step: compile ``csrc/bi_attn.hip`` for gfx950 into ``libbiattn.so`` (in-tree)."""
+"""Build step: compile ``csrc/bi_attn.hip`` and ``csrc/bi_norm.hip`` for gfx950 into
+``libbiattn.so`` (in-tree)."""
 
 from __future__ import annotations
 
@@ -8,7 +9,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "bi_attn.hip")
+SRCS = [os.path.join(HERE, "csrc", "bi_attn.hip"), os.path.join(HERE, "csrc", "bi_norm.hip")]
 OUT = os.path.join(HERE, "libbiattn.so")
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out explicitly, so the
@@ -30,7 +31,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile the library (always recompiles) and return its path."""
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

@@ -11,3 +11,4 @@ from .attention import (  # noqa: F401
     fold,
     split_fold_attention,
 )
+from .rmsnorm import rmsnorm  # noqa: F401,E402

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for batch-invariant paged attention.
+"""Seeded synthetic inputs for batch-invariant paged attention (and RMSNorm).
 
 This package generates inputs only: token values, page placements, batches and the
 mixed continuous-batching schedule. It holds none of the attention arithmetic, so the
@@ -20,4 +20,5 @@ from .workloads import (  # noqa: F401
     Trace,
     PageAllocator,
     CONFIG_SHAPES,
+    norm_inputs,
 )

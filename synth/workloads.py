@@ -327,3 +327,17 @@ class PageAllocator:
 
     def release(self, req: int) -> None:
         self.free.extend(self.owned.pop(req, []))
+
+
+# ----------------------------------------------------------------------------- RMSNorm inputs
+def norm_inputs(seed: int, rows: int, hidden: int, dtype: str):
+    """Seeded RMSNorm inputs: activations ``x [rows][hidden]`` ~ N(0,1) and a weight vector
+    ``[hidden]`` ~ U[0.5, 1.5], as float32 arrays holding values exact in ``dtype``. Row r's
+    values depend on (seed, r) only, so a row is the same whatever rows surround it."""
+    x = np.empty((rows, hidden), np.float32)
+    for r in range(rows):
+        x[r] = np.random.default_rng([int(seed), 0x4E4F, r]).standard_normal(hidden)
+    w = np.random.default_rng([int(seed), 0x5747]).uniform(0.5, 1.5, hidden).astype(np.float32)
+    if dtype == "bf16":
+        x, w = bf16_round(x), bf16_round(w)
+    return x, w

@@ -1,9 +1,10 @@
-"""The C-ABI library loads, exports what include/bi_attn.h declares, and validates arguments.
+"""The C-ABI library loads, exports what include/*.h declare, and validates arguments.
 
 CPU only: every call below fails validation, so nothing is ever launched.
 """
 
 import ctypes
+import glob
 import os
 import re
 
@@ -12,13 +13,15 @@ import pytest
 import invariant_attention_amd as bi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bi_attn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bi_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(bi_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
