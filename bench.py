@@ -364,6 +364,42 @@ def run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref):
     log(f"varlen (dense K/V): {result['varlen']['kernel_tflops']:.1f} TFLOP/s, same bits as paged")
 
 
+# ----------------------------------------------------------------------------- RMSNorm
+def run_rmsnorm_bench(args, result):
+    """Batch-invariant RMSNorm of a 16384-token activation block (hidden 4096, bf16): HBM GB/s
+    (x read once, y written once, the weight once), and row bits at 1 vs 16384 rows."""
+    from synth import norm_inputs
+    rows, hidden = 16384, 4096
+    x, w = norm_inputs(2030, rows, hidden, "bf16")
+    xs = [dev(x, torch.bfloat16) for _ in range(2)]     # two copies, alternated across launches
+    wd = dev(w, torch.bfloat16)
+    y = torch.empty_like(xs[0])
+    bi.bi_rmsnorm(xs[0], wd, y, 1e-6)
+    y1 = torch.empty((1, hidden), dtype=torch.bfloat16, device="cuda")
+    for r in (0, 7777, rows - 1):
+        bi.bi_rmsnorm(xs[0][r:r + 1].contiguous(), wd, y1, 1e-6)
+        assert torch.equal(y1.view(torch.int16), y[r:r + 1].view(torch.int16)), "rmsnorm row bits"
+    n = max(10, args.steps)
+    for i in range(3):
+        bi.bi_rmsnorm(xs[i % 2], wd, y, 1e-6)
+    tm = Timer(2)
+    torch.cuda.synchronize()
+    tm.mark(0)
+    for i in range(n):
+        bi.bi_rmsnorm(xs[i % 2], wd, y, 1e-6)
+    tm.mark(1)
+    torch.cuda.synchronize()
+    ms = tm.ms(0, 1) / n
+    nbytes = 2 * rows * hidden * 2 + hidden * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    result["rmsnorm"] = {"value": gbs, "unit": "GB/s", "ms": ms, "bytes": nbytes,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
+                         "bits": "rows 0, 7777, 16383 alone equal to the 16384-row call",
+                         "config": {"workload": "rmsnorm_bf16: 16384 rows x hidden 4096, eps 1e-6"}}
+    log(f"rmsnorm: {gbs:.0f} GB/s ({ms * 1e3:.1f} us for {nbytes / 1e6:.0f} MB)")
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(result, bt_dec, gpu_dec, samples):
     """Time the fp64 oracle on the host and use its outputs for the parity check."""
@@ -454,6 +490,8 @@ def main():
     if not args.no_prefill:
         run_prefill_bench(args, result)
         log(f"prefill: {result['prefill']['kernel_tflops']:.1f} TFLOP/s (kernel)")
+    if not args.profile_run:
+        run_rmsnorm_bench(args, result)
     if not args.no_cpu_baseline:
         cpu_baseline(result, bt_dec, gpu_dec, args.cpu_samples)
     print(json.dumps(result), flush=True)

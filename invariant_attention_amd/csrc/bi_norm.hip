@@ -6,8 +6,8 @@
 // wavefront: row r is read, reduced and written by one wave, which never exchanges data with
 // another, so the bits of a row cannot depend on how many rows there are.
 //
-// HBM-bound: a row is read once (kept in registers up to kCache 16-byte chunks per lane, read
-// again from L2/HBM past that) and written once.
+// HBM-bound: a row is read once (kept in registers up to kCache 16-byte chunks per lane, with
+// the matching weight chunks; read again from L2/HBM past that) and written once.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -18,7 +18,7 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNormWaves = 4;      // waves (rows in flight) per workgroup
-constexpr int kCache = 16;         // 16-byte chunks per lane kept in registers (8 KB rows of bf16)
+constexpr int kCache = 8;          // 16-byte chunks per lane kept in registers (8 KB rows of bf16)
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -77,16 +77,19 @@ __global__ __launch_bounds__(64 * kNormWaves) void rmsnorm_kernel(const char* x,
     const u32x4* xr = (const u32x4*)(x + (size_t)r * chunks * 16);
     u32x4* yr = (u32x4*)(y + (size_t)r * chunks * 16);
     // lane's chunks lane, lane + 64, ...: squares summed in that order
-    u32x4 xc[kCache];
-    float s = 0.f;
+    u32x4 xc[kCache], wc[kCache];
 #pragma unroll
     for (int k = 0; k < kCache; ++k) {
       const int ch = lane + 64 * k;
       if (ch < chunks) {
         xc[k] = xr[ch];
-        s += chunk_sq<BF>(xc[k]);
+        wc[k] = ((const u32x4*)w)[ch];
       }
     }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCache; ++k)
+      if (lane + 64 * k < chunks) s += chunk_sq<BF>(xc[k]);
     for (int ch = lane + 64 * kCache; ch < chunks; ch += 64) s += chunk_sq<BF>(xr[ch]);
     // fixed butterfly over the 64 lanes: every lane ends with the same total
 #pragma unroll
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(64 * kNormWaves) void rmsnorm_kernel(const char* x,
 #pragma unroll
     for (int k = 0; k < kCache; ++k) {
       const int ch = lane + 64 * k;
-      if (ch < chunks) yr[ch] = chunk_out<BF>(xc[k], ((const u32x4*)w)[ch], rs);
+      if (ch < chunks) yr[ch] = chunk_out<BF>(xc[k], wc[k], rs);
     }
     for (int ch = lane + 64 * kCache; ch < chunks; ch += 64) yr[ch] = chunk_out<BF>(xr[ch], ((const u32x4*)w)[ch], rs);
   }
