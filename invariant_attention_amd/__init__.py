@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     bi_attn_decode,
+    bi_gemm,
     bi_attn_decode_combine,
     bi_attn_decode_partials,
     bi_attn_prefill,

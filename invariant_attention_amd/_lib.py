@@ -24,7 +24,7 @@ BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode",
             "bi_attn_decode_partials", "bi_attn_decode_combine", "bi_attn_prefill",
-            "bi_attn_varlen", "bi_status_string", "bi_rmsnorm")
+            "bi_attn_varlen", "bi_status_string", "bi_rmsnorm", "bi_gemm")
 
 
 class BiAttnError(RuntimeError):
@@ -92,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.bi_attn_prefill.argtypes = [CP, P, P, P, P, I, I, P, P, I, I, I, I, P, P, Z, P]
     lib.bi_attn_varlen.restype = ctypes.c_int
     lib.bi_rmsnorm.restype = ctypes.c_int
+    lib.bi_gemm.restype = ctypes.c_int
+    lib.bi_gemm.argtypes = [P, P, P, I, I, I, I, P]
     lib.bi_rmsnorm.argtypes = [P, P, P, I, I, I, ctypes.c_float, P]
     lib.bi_attn_varlen.argtypes = [CP, P, P, P, P, P, I, I, I, I, I, P, P]
     _lib = lib
@@ -205,3 +207,15 @@ def bi_rmsnorm(x: torch.Tensor, weight: torch.Tensor, y: torch.Tensor, eps: floa
                            BI_BF16 if x.dtype == torch.bfloat16 else BI_F32, float(eps),
                            _stream(stream))
     _check(st, "bi_rmsnorm")
+
+
+def bi_gemm(a: torch.Tensor, w: torch.Tensor, c: torch.Tensor, stream=None) -> None:
+    """Batch-invariant ``c = a @ w.T``: ``a [M][K]``, ``w [N][K]`` bf16, ``c [M][N]`` fp32 or
+    bf16; N a multiple of 128, K a multiple of 64."""
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or c.dtype not in (torch.float32, torch.bfloat16):
+        raise BiAttnError(BI_EINVAL, "bi_gemm")
+    if a.shape[1] != w.shape[1] or c.shape[0] != a.shape[0] or c.shape[1] != w.shape[0]:
+        raise BiAttnError(BI_EINVAL, "bi_gemm")
+    st = load().bi_gemm(_ptr(a), _ptr(w), _ptr(c), a.shape[0], w.shape[0], a.shape[1],
+                        1 if c.dtype == torch.bfloat16 else 0, _stream(stream))
+    _check(st, "bi_gemm")

@@ -1,5 +1,5 @@
-"""Build step: compile ``csrc/bi_attn.hip`` and ``csrc/bi_norm.hip`` for gfx950 into
-``libbiattn.so`` (in-tree)."""
+"""Build step: compile ``csrc/bi_attn.hip``, ``csrc/bi_norm.hip`` and ``csrc/bi_gemm.hip`` for
+gfx950 into ``libbiattn.so`` (in-tree)."""
 
 from __future__ import annotations
 
@@ -9,7 +9,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "bi_attn.hip"), os.path.join(HERE, "csrc", "bi_norm.hip")]
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("bi_attn.hip", "bi_norm.hip", "bi_gemm.hip")]
 OUT = os.path.join(HERE, "libbiattn.so")
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out explicitly, so the

@@ -12,3 +12,4 @@ from .attention import (  # noqa: F401
     split_fold_attention,
 )
 from .rmsnorm import rmsnorm  # noqa: F401,E402
+from .gemm import gemm  # noqa: F401,E402

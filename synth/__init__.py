@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for batch-invariant paged attention (and RMSNorm).
+"""Seeded synthetic inputs for batch-invariant paged attention (and RMSNorm and GEMM).
 
 This package generates inputs only: token values, page placements, batches and the
 mixed continuous-batching schedule. It holds none of the attention arithmetic, so the
@@ -21,4 +21,5 @@ from .workloads import (  # noqa: F401
     PageAllocator,
     CONFIG_SHAPES,
     norm_inputs,
+    gemm_inputs,
 )

@@ -341,3 +341,14 @@ def norm_inputs(seed: int, rows: int, hidden: int, dtype: str):
     if dtype == "bf16":
         x, w = bf16_round(x), bf16_round(w)
     return x, w
+
+
+# ----------------------------------------------------------------------------- GEMM inputs
+def gemm_inputs(seed: int, m: int, n: int, k: int):
+    """Seeded linear-layer inputs: activations ``A [m][k]`` ~ N(0,1) (row i depends on (seed, i)
+    only) and a weight ``W [n][k]`` ~ N(0, 1/k), as float32 arrays holding bf16 values."""
+    a = np.empty((m, k), np.float32)
+    for i in range(m):
+        a[i] = np.random.default_rng([int(seed), 0x4745, i]).standard_normal(k)
+    w = (np.random.default_rng([int(seed), 0x5745]).standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
+    return bf16_round(a), bf16_round(w)

@@ -1,0 +1,72 @@
+"""Batch-invariant GEMM on the GPU: parity with the fp64 oracle within the fp32 summation bound,
+and zero differing bits across M (GPU)."""
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_attention_amd as bi
+import oracle
+from synth import gemm_inputs
+from gpu_harness import assert_bitwise
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def run(a, w, out_dtype=torch.float32):
+    c = torch.full((a.shape[0], w.shape[0]), float("nan"), dtype=out_dtype, device="cuda")
+    bi.bi_gemm(a, w, c)
+    torch.cuda.synchronize()
+    return c
+
+
+def check(c, a, w, what):
+    """fp32 accumulation of K exact products (bf16 x bf16 fits fp32): |err| <= K 2^-24 (|A| |W|^T)
+    in any summation order; a bf16 result adds its rounding, at most half a unit of an 8-bit
+    significand: 2^-8 times the fp32 value."""
+    ref = oracle.gemm(a, w)
+    bound = a.shape[1] * 2.0 ** -24 * (np.abs(a).astype(np.float64) @ np.abs(w).astype(np.float64).T) + 1e-30
+    got = c.float().cpu().numpy().astype(np.float64)
+    if c.dtype == torch.bfloat16:
+        bound = bound + 2.0 ** -8 * (np.abs(ref) + bound)
+    assert np.isfinite(got).all(), what
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements past the bound"
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("m,n,k", [(1, 128, 64), (5, 256, 128), (128, 128, 4096), (300, 384, 576),
+                                   (257, 1024, 1024)])
+def test_gemm_parity(out, m, n, k):
+    print("CASE gemm", out, m, n, k, flush=True)
+    a, w = gemm_inputs(51, m, n, k)
+    ad, wd = torch.from_numpy(a).cuda().to(torch.bfloat16), torch.from_numpy(w).cuda().to(torch.bfloat16)
+    c = run(ad, wd, torch.bfloat16 if out == "bf16" else torch.float32)
+    check(c, a, w, f"gemm {out} {m}x{n}x{k}")
+
+
+def test_gemm_rows_are_batch_invariant():
+    """A row's outputs do not depend on M (the token count) or the row's position."""
+    m, n, k = 1000, 512, 2048
+    print("CASE gemm invariance", flush=True)
+    a, w = gemm_inputs(52, m, n, k)
+    ad, wd = torch.from_numpy(a).cuda().to(torch.bfloat16), torch.from_numpy(w).cuda().to(torch.bfloat16)
+    full = run(ad, wd)
+    for rows in (1, 3, 127, 128, 129, 600):
+        assert_bitwise(run(ad[:rows].contiguous(), wd), full[:rows], f"first {rows} rows")
+    perm = torch.randperm(m, generator=torch.Generator().manual_seed(4)).cuda()
+    assert_bitwise(run(ad[perm].contiguous(), wd), full[perm], "permuted rows")
+    for r in (0, 500, 999):
+        assert_bitwise(run(ad[r:r + 1].contiguous(), wd), full[r:r + 1], f"row {r} alone")
+    fb = run(ad, wd, torch.bfloat16)
+    assert_bitwise(run(ad[7:8].contiguous(), wd, torch.bfloat16), fb[7:8], "bf16 output row")
+
+
+def test_gemm_rejects_bad_sizes():
+    a = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bi.BiAttnError):
+        run(a, torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda"))    # N % 128
+    with pytest.raises(bi.BiAttnError):
+        run(torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda"),
+            torch.zeros((128, 96), dtype=torch.bfloat16, device="cuda"))       # K % 64
