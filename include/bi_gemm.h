@@ -27,7 +27,7 @@ extern "C" {
  * 32x32x16 k-substeps in ascending order: no split of K, the same tiles and order for every M,
  * so C[i][j] depends on row i of A and row j of W only.
  * c_dtype: 0 = fp32, 1 = bf16 (round to nearest even). Sizes: M >= 0 any; N a positive multiple
- * of 128; K a positive multiple of 64. A, W, C: device memory, row-major, 16-byte aligned,
+ * of 128; K a positive multiple of 64 below 2^22. A, W, C: device memory, row-major, 16-byte aligned,
  * caller-owned; C must not overlap A or W. Returns 0 (ok), 1 (invalid argument), 2 (unsupported
  * size) with nothing launched, or 4 when the launch fails. M == 0 launches nothing.
  */
