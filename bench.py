@@ -400,6 +400,53 @@ def run_rmsnorm_bench(args, result):
     log(f"rmsnorm: {gbs:.0f} GB/s ({ms * 1e3:.1f} us for {nbytes / 1e6:.0f} MB)")
 
 
+# ----------------------------------------------------------------------------- GEMM
+def run_gemm_bench(args, result):
+    """Batch-invariant GEMM C = A W^T on a linear-layer shape (8192 tokens, 4096 -> 8192, bf16),
+    against torch.matmul (hipBLASLt) on the same tensors; row bits at M = 1 vs M = 8192."""
+    m, n, k = 8192, 8192, 4096
+    g = torch.Generator(device="cuda").manual_seed(2031)
+    a = torch.randn((m, k), device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn((n, k), device="cuda", generator=g) / 64).to(torch.bfloat16)
+    c = torch.empty((m, n), device="cuda", dtype=torch.bfloat16)
+    bi.bi_gemm(a, w, c)
+    c1 = torch.empty((1, n), device="cuda", dtype=torch.bfloat16)
+    for r in (0, 4097, m - 1):
+        bi.bi_gemm(a[r:r + 1].contiguous(), w, c1)
+        assert torch.equal(c1.view(torch.int16), c[r:r + 1].view(torch.int16)), "gemm row bits"
+    ref_full = torch.matmul(a, w.t())
+    vendor_same = all(torch.equal(torch.matmul(a[r:r + 1], w.t()).view(torch.int16),
+                                  ref_full[r:r + 1].view(torch.int16)) for r in (0, 4097, m - 1))
+
+    def timed(fn, n_it):
+        for _ in range(3):
+            fn()
+        tm = Timer(2)
+        torch.cuda.synchronize()
+        tm.mark(0)
+        for _ in range(n_it):
+            fn()
+        tm.mark(1)
+        torch.cuda.synchronize()
+        return tm.ms(0, 1) / n_it
+
+    n_it = max(10, args.steps // 2)
+    ms = timed(lambda: bi.bi_gemm(a, w, c), n_it)
+    ms_v = timed(lambda: torch.matmul(a, w.t(), out=c), n_it)
+    fl = 2.0 * m * n * k
+    tf, tf_v = fl / (ms * 1e-3) / 1e12, fl / (ms_v * 1e-3) / 1e12
+    result["gemm"] = {"value": tf, "unit": "TFLOP/s", "ms": ms,
+                      "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS},
+                      "vs_hipblaslt": {"hipblaslt_tflops": tf_v, "ratio": tf / tf_v,
+                                       "hipblaslt_rows_same_bits_at_m1": vendor_same},
+                      "bits": "rows 0, 4097, 8191 at M = 1 equal to the M = 8192 call",
+                      "config": {"workload": "gemm_bf16: C[8192][8192] = A[8192][4096] W[8192][4096]^T, "
+                                             "bf16 in and out, fp32 accumulation"}}
+    log(f"gemm: {tf:.0f} TFLOP/s ({tf / tf_v:.2f}x hipBLASLt {tf_v:.0f}; hipBLASLt rows same bits "
+        f"at M = 1: {vendor_same})")
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(result, bt_dec, gpu_dec, samples):
     """Time the fp64 oracle on the host and use its outputs for the parity check."""
@@ -492,6 +539,7 @@ def main():
         log(f"prefill: {result['prefill']['kernel_tflops']:.1f} TFLOP/s (kernel)")
     if not args.profile_run:
         run_rmsnorm_bench(args, result)
+        run_gemm_bench(args, result)
     if not args.no_cpu_baseline:
         cpu_baseline(result, bt_dec, gpu_dec, args.cpu_samples)
     print(json.dumps(result), flush=True)
