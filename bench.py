@@ -43,23 +43,25 @@ def log(*a):
 
 KERNEL_SOURCES = ("invariant_attention_amd/csrc/bi_attn.hip", "invariant_attention_amd/csrc/core.hpp",
                   "include/bi_attn.h")
+NORM_SOURCES = ("invariant_attention_amd/csrc/bi_norm.hip", "include/bi_norm.h")
+GEMM_SOURCES = ("invariant_attention_amd/csrc/bi_gemm.hip", "include/bi_gemm.h")
 
 
-def kernel_sha256():
+def kernel_sha256(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def profiled_traffic(kernel):
+def profiled_traffic(kernel, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summaries, if they were taken
     on the kernel sources as they are now (else None)."""
     import glob
     import re
-    sha = kernel_sha256()
+    sha = kernel_sha256(sources)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for m in re.finditer(r"<!-- traffic: (\{.*?\}) -->", open(path).read()):
             rec = json.loads(m.group(1))
@@ -394,7 +396,8 @@ def run_rmsnorm_bench(args, result):
     gbs = nbytes / (ms * 1e-3) / 1e9
     result["rmsnorm"] = {"value": gbs, "unit": "GB/s", "ms": ms, "bytes": nbytes,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
+                                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                      "traffic": profiled_traffic("rmsnorm_kernel", NORM_SOURCES)},
                          "bits": "rows 0, 7777, 16383 alone equal to the 16384-row call",
                          "config": {"workload": "rmsnorm_bf16: 16384 rows x hidden 4096, eps 1e-6"}}
     log(f"rmsnorm: {gbs:.0f} GB/s ({ms * 1e3:.1f} us for {nbytes / 1e6:.0f} MB)")
@@ -437,7 +440,9 @@ def run_gemm_bench(args, result):
     tf, tf_v = fl / (ms * 1e-3) / 1e12, fl / (ms_v * 1e-3) / 1e12
     result["gemm"] = {"value": tf, "unit": "TFLOP/s", "ms": ms,
                       "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS},
+                                   "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                                   "traffic": profiled_traffic("gemm_kernel", GEMM_SOURCES)},
+                      "bytes": 2 * (m * k + n * k + m * n),
                       "vs_hipblaslt": {"hipblaslt_tflops": tf_v, "ratio": tf / tf_v,
                                        "hipblaslt_rows_same_bits_at_m1": vendor_same},
                       "bits": "rows 0, 4097, 8191 at M = 1 equal to the M = 8192 call",
@@ -498,6 +503,8 @@ def main():
     ap.add_argument("--profile-run", action="store_true",
                     help="only the headline decode steps and the prefill workload (no split-by-batch "
                          "variant, no batch sweep), so a profiler sees one workload per kernel")
+    ap.add_argument("--next-rows-only", action="store_true",
+                    help="only the RMSNorm and GEMM legs (no headline value; for profiling those kernels)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -525,6 +532,11 @@ def main():
         torch.cuda.synchronize()
         result["copy_calib_bytes"] = n
         del src, dst
+    if args.next_rows_only:
+        run_rmsnorm_bench(args, result)
+        run_gemm_bench(args, result)
+        print(json.dumps(result), flush=True)
+        return
     if args.prefill_only:
         result["variant_slowdown"] = {}
         run_prefill_bench(args, result)
