@@ -1,20 +1,21 @@
-// bi_gemm.hip — batch-invariant GEMM C = A W^T (gfx950): fixed 128 x 128 output tiles, the whole
-// of K inside one workgroup in ascending order, MFMA 32x32x16 bf16.
+// bi_gemm.hip — batch-invariant GEMM C = A W^T (gfx950): fixed output tiles (128 x 128, or
+// 256 x 256 for large products), the whole of K inside one workgroup in ascending order, MFMA
+// 32x32x16 bf16.
 //
 // The matmul is made batch invariant by a fixed tile configuration with no Split-K (xitu-tech.com
 // report, section 构建确定性解决方案, matrix multiplication item): the output is cut into 2-D tiles
 // and each core finishes its dot products itself (neican.ai insight page, section
-// 技术原理与创新点解析, matmul item). Here a workgroup owns one 128 x 128 tile of C and reduces
-// all of K for it; the order of a C element's products (64-wide K steps ascending, 16-wide MFMA
-// k-substeps ascending inside a step) is the same for every M and every tile position.
+// 技术原理与创新点解析, matmul item). Here a workgroup owns one tile of C and reduces all of K
+// for it; the order of a C element's products (16-wide MFMA k-substeps, ascending, each into the
+// one fp32 accumulator) is the same for every M, every tile shape and every tile position.
 //
 // Data path: A and W tiles go HBM -> LDS by buffer loads to LDS (buffer_load_dwordx4 ... lds: no
 // register staging; a scalar resource per operand tile and 32-bit lane offsets; the compiler
 // counts them on the vector-memory counter only, so the operand reads wait for just what they
 // need, where a global_load_lds would turn each wait into a wait for every LDS read in flight:
-// 12-18% faster here), two buffers as separate LDS variables, one barrier per K step. LDS rows are 64 bf16 (128 bytes);
-// the 16-byte chunk c of row R sits at chunk c ^ ((R >> 1) & 7), so the operand reads (32 rows
-// at one chunk, eight lanes at a time) hit distinct banks.
+// 12-18% faster here), two buffers as separate LDS variables, one barrier per K step. LDS rows
+// are BK bf16; a row's 16-byte chunks are permuted by phys_chunk so that the operand reads (32
+// rows at one chunk) hit distinct banks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,24 +28,31 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BK = 64;                           // K step
+constexpr int kKAlign = 64;                      // K must be a multiple of this
 constexpr int kThreadsG = 256;                   // 4 waves in a 2 x 2 grid
 constexpr int kWaitVm0 = 0x0F70;                 // s_waitcnt vmcnt(0)
 // A wave computes TM x TN MFMA tiles of 32 x 32 (rows x columns of C); the workgroup tile is
-// BM x BN = 64 TM x 64 TN. The tile shape changes no element's order of products.
-template <int TM, int TN> struct GemmTile {
+// BM x BN = 64 TM x 64 TN, staged BK columns of K at a time. Neither the tile shape nor BK
+// changes any element's order of products (16-wide MFMA k-substeps, ascending).
+template <int TM, int TN, int BK_> struct GemmTile {
+  static constexpr int BK = BK_, CPR = BK / 8;   // 16-byte chunks per LDS row
   static constexpr int BM = 64 * TM, BN = 64 * TN;
   static constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2;
-  static constexpr int A_ROUNDS = BM * 8 / kThreadsG, W_ROUNDS = BN * 8 / kThreadsG;
+  static constexpr int A_ROUNDS = BM * CPR / kThreadsG, W_ROUNDS = BN * CPR / kThreadsG;
 };
 
-__device__ __forceinline__ int phys_chunk(int c, int row) { return c ^ ((row >> 1) & 7); }
+// Chunk c of LDS row R is stored at chunk phys_chunk(c, R): the 16 rows that one pass of a
+// 16-byte operand read touches (one chunk each) then fall on 16 distinct 16-byte bank groups.
+template <int CPR> __device__ __forceinline__ int phys_chunk(int c, int row) {
+  if constexpr (CPR == 8) return c ^ ((row >> 1) & 7);
+  else return c ^ ((row >> 2) & 3);
+}
 
-template <bool OUT_BF16, int TM, int TN, int MINB>
+template <bool OUT_BF16, int TM, int TN, int BK, int MINB>
 __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, const char* W, char* C, int M,
                                                               int N, int K) {
-  using T = GemmTile<TM, TN>;
-  constexpr int BM = T::BM, BN = T::BN;
+  using T = GemmTile<TM, TN, BK>;
+  constexpr int BM = T::BM, BN = T::BN, CPR = T::CPR, KS = BK / 16;
   __shared__ __attribute__((aligned(16))) char a0[T::A_BYTES];   // even K steps
   __shared__ __attribute__((aligned(16))) char w0[T::W_BYTES];
   __shared__ __attribute__((aligned(16))) char a1[T::A_BYTES];   // odd K steps
@@ -56,19 +64,19 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
   const int m0 = tm * BM, n0 = tn * BN;
   const size_t rowb = (size_t)K * 2;               // bytes per row of A and W
 
-  // DMA: slot p = 256 t + 64 wave + lane of a tile is LDS row p / 8, physical chunk p % 8, which
-  // holds logical chunk (p % 8) ^ ((row >> 1) & 7) of that row. Rows of A past M read row M - 1
+  // DMA: slot p = 256 t + 64 wave + lane of a tile is LDS row p / CPR, physical chunk p % CPR,
+  // which holds the logical chunk that phys_chunk maps there (phys_chunk is an involution). Rows of A past M read row M - 1
   // (their outputs are not written).
   unsigned a_vo[T::A_ROUNDS], w_vo[T::W_ROUNDS];
 #pragma unroll
   for (int t = 0; t < T::A_ROUNDS; ++t) {
-    const int p = 256 * t + 64 * wave + lane, R = p >> 3;
-    a_vo[t] = (unsigned)((min(m0 + R, M - 1) - m0) * rowb) + phys_chunk(p & 7, R) * 16;
+    const int p = 256 * t + 64 * wave + lane, R = p / CPR;
+    a_vo[t] = (unsigned)((min(m0 + R, M - 1) - m0) * rowb) + phys_chunk<CPR>(p % CPR, R) * 16;
   }
 #pragma unroll
   for (int t = 0; t < T::W_ROUNDS; ++t) {
-    const int p = 256 * t + 64 * wave + lane, R = p >> 3;
-    w_vo[t] = (unsigned)(R * rowb) + phys_chunk(p & 7, R) * 16;
+    const int p = 256 * t + 64 * wave + lane, R = p / CPR;
+    w_vo[t] = (unsigned)(R * rowb) + phys_chunk<CPR>(p % CPR, R) * 16;
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
   // (the buffer builtins exist only in the device pass; the host pass never runs this body)
@@ -91,19 +99,19 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
   // operand reads: A rows (BM / 2) wm + 32 i + lane % 32, W rows (BN / 2) wn + 32 j + lane % 32,
   // logical chunk 2 ks + lane / 32 (k = 16 ks + 8 (lane / 32) .. + 7)
   const int wm = wave & 1, wn = wave >> 1;
-  unsigned rd_a[TM][4], rd_w[TN][4];
+  unsigned rd_a[TM][KS], rd_w[TN][KS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const int c = 2 * ks + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int ra = (BM / 2) * wm + 32 * i + (lane & 31);
-      rd_a[i][ks] = (unsigned)(ra * 128 + phys_chunk(c, ra) * 16);
+      rd_a[i][ks] = (unsigned)(ra * BK * 2 + phys_chunk<CPR>(c, ra) * 16);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int rw = (BN / 2) * wn + 32 * j + (lane & 31);
-      rd_w[j][ks] = (unsigned)(rw * 128 + phys_chunk(c, rw) * 16);
+      rd_w[j][ks] = (unsigned)(rw * BK * 2 + phys_chunk<CPR>(c, rw) * 16);
     }
   }
 
@@ -122,8 +130,8 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
 #pragma unroll
     for (int j = 0; j < TN; ++j) w[j] = *(const u32x4*)&sw[rd_w[j][0]];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) {
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) an[i] = *(const u32x4*)&sa[rd_a[i][ks + 1]];
 #pragma unroll
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
                                                               __builtin_bit_cast(bf16x8, w[j]), acc[i][j], 0, 0, 0);
-      if (ks + 1 < 4) {
+      if (ks + 1 < KS) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) a[i] = an[i];
 #pragma unroll
@@ -149,17 +157,18 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
   dma(0, a0, w0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
-    if (kt + 1 < KT) dma(kt + 1, a1, w1);
+  // pairs of K steps (one loop exit, so the accumulators stay in place), then an odd last step
+  for (int kt = 0; kt + 1 < KT; kt += 2) {
+    dma(kt + 1, a1, w1);
     compute(a0, w0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    if (kt + 1 >= KT) break;
     if (kt + 2 < KT) dma(kt + 2, a0, w0);
     compute(a1, w1);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }
+  if (KT & 1) compute(a0, w0);
 
   // epilogue: element e of acc[i][j] is C row (BM / 2) wm + 32 i + 8 (e / 4) + 4 (lane / 32) +
   // e % 4, column (BN / 2) wn + 32 j + lane % 32
@@ -181,25 +190,25 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-#ifndef GEMM_TM
-#define GEMM_TM 2
-#endif
-#ifndef GEMM_TN
-#define GEMM_TN 2
-#endif
+// Large products take 256 x 256 workgroup tiles (one workgroup per CU, 128 x 128 per wave: half
+// the LDS operand reads and half the fabric traffic per flop of the 128 x 128 tile); products
+// with fewer than kBigTilesMin such tiles take 128 x 128 tiles, so the grid still fills the chip.
+// Both walk every element's K in the same 16-wide MFMA steps, so their bits are identical and
+// the choice (which depends on M) cannot make a row's result depend on M.
+constexpr int kBigTilesMin = 256;
 
-template <int TM, int TN>
+template <int TM, int TN, int BK>
 int launch_gemm(const void* a, const void* w, void* c, int m, int n, int k, int c_dtype, hipStream_t stream) {
-  using T = GemmTile<TM, TN>;
+  using T = GemmTile<TM, TN, BK>;
   constexpr int MINB = (2 * (T::A_BYTES + T::W_BYTES) <= 80 * 1024) ? 2 : 1;
   if (n % T::BN) return 2;
   const int64_t tiles = (((int64_t)m + T::BM - 1) / T::BM) * (n / T::BN);
   if (tiles > 0x7fffffff) return 2;
   if (c_dtype == 1)
-    hipLaunchKernelGGL((gemm_kernel<true, TM, TN, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<true, TM, TN, BK, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
                        (const char*)a, (const char*)w, (char*)c, m, n, k);
   else
-    hipLaunchKernelGGL((gemm_kernel<false, TM, TN, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<false, TM, TN, BK, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
                        (const char*)a, (const char*)w, (char*)c, m, n, k);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
@@ -210,9 +219,11 @@ extern "C" int bi_gemm(const void* a, const void* w, void* c, int32_t m, int32_t
                        int32_t c_dtype, hipStream_t stream) {
   if (c_dtype != 0 && c_dtype != 1) return 1;
   if (m < 0 || n <= 0 || k <= 0) return 1;
-  if (n % 128 || k % BK) return 2;
+  if (n % 128 || k % kKAlign) return 2;
   if ((int64_t)k * 2 * 256 >= ((int64_t)1 << 31)) return 2;   // 32-bit lane offsets inside a tile
   if (m == 0) return 0;
   if (!a || !w || !c || !aligned16(a) || !aligned16(w) || !aligned16(c)) return 1;
-  return launch_gemm<GEMM_TM, GEMM_TN>(a, w, c, m, n, k, c_dtype, stream);
+  const int64_t big_tiles = (((int64_t)m + 255) / 256) * (n / 256);
+  if (n % 256 == 0 && big_tiles >= kBigTilesMin) return launch_gemm<4, 4, 64>(a, w, c, m, n, k, c_dtype, stream);
+  return launch_gemm<2, 2, 64>(a, w, c, m, n, k, c_dtype, stream);
 }

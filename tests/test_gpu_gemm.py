@@ -70,3 +70,30 @@ def test_gemm_rejects_bad_sizes():
     with pytest.raises(bi.BiAttnError):
         run(torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda"),
             torch.zeros((128, 96), dtype=torch.bfloat16, device="cuda"))       # K % 64
+
+
+@pytest.mark.parametrize("m,k", [(2048, 256), (2085, 320)])
+def test_gemm_large_tile_parity(m, k):
+    """Shapes with at least 256 tiles of 256 x 256 take the large tile (M = 2085: a ragged last
+    tile row; K = 320: an odd number of 64-wide K steps): same bound against the oracle."""
+    n = 8192
+    print("CASE gemm large tile", m, flush=True)
+    a, w = gemm_inputs(53, m, n, k)
+    ad, wd = torch.from_numpy(a).cuda().to(torch.bfloat16), torch.from_numpy(w).cuda().to(torch.bfloat16)
+    check(run(ad, wd), a, w, f"gemm f32 {m}x{n}x{k}")
+    check(run(ad, wd, torch.bfloat16), a, w, f"gemm bf16 {m}x{n}x{k}")
+
+
+def test_gemm_rows_same_bits_across_tile_shapes():
+    """Rows of a product that takes the 256 x 256 tiles equal, bit for bit, the same rows computed
+    in products small enough to take the 128 x 128 tiles (M = 1, 7, 300)."""
+    m, n, k = 2085, 8192, 512
+    print("CASE gemm tile shapes", flush=True)
+    a, w = gemm_inputs(54, m, n, k)
+    ad, wd = torch.from_numpy(a).cuda().to(torch.bfloat16), torch.from_numpy(w).cuda().to(torch.bfloat16)
+    for out in (torch.float32, torch.bfloat16):
+        full = run(ad, wd, out)
+        assert_bitwise(run(ad[:300].contiguous(), wd, out), full[:300], f"first 300 rows {out}")
+        assert_bitwise(run(ad[2078:].contiguous(), wd, out), full[2078:], f"last 7 rows {out}")
+        for r in (0, 1041, 2084):
+            assert_bitwise(run(ad[r:r + 1].contiguous(), wd, out), full[r:r + 1], f"row {r} alone {out}")
