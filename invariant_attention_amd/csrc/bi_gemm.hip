@@ -188,13 +188,97 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
     }
 }
 
+// Skinny products (few rows of A): one wave per workgroup owns a 32 TM x 32 tile of C and loads
+// its A and W operands straight into registers, P 16-wide k-substeps ahead of the MFMA that uses
+// them (a ring of P operand sets, so that enough bytes of W are in flight with only N / 32 waves);
+// no LDS, no barrier. Lane l loads, for k-substep s, the 16 bytes k = 16 s + 8 (l / 32) .. + 7 of
+// A row 32 i + l % 32 (rows past M read row M - 1) and of W row l % 32 of the tile: the operands,
+// MFMA and accumulation order of the tiled kernel above, so every element has the same bits.
+template <bool OUT_BF16, int TM, int P>
+__global__ __launch_bounds__(64) void gemm_skinny_kernel(const char* A, const char* W, char* C, int M, int N,
+                                                         int K) {
+  const int lane = threadIdx.x;
+  const int n0 = (int)blockIdx.x * 32, m0 = (int)blockIdx.y * 32 * TM;
+  const size_t rowb = (size_t)K * 2;
+  const int ks_total = K / 16;
+  const char* wrow = W + (size_t)(n0 + (lane & 31)) * rowb + (lane >> 5) * 16;
+  const char* arow[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) arow[i] = A + (size_t)min(m0 + 32 * i + (lane & 31), M - 1) * rowb + (lane >> 5) * 16;
+  u32x4 wr[P], ar[P][TM];
+  // substep s lives in slot s % P; loads past the last substep re-read it (never used)
+  auto load = [&](int slot, int s) __attribute__((always_inline)) {
+    const size_t off = (size_t)min(s, ks_total - 1) * 32;
+    wr[slot] = *(const u32x4*)(wrow + off);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ar[slot][i] = *(const u32x4*)(arow[i] + off);
+  };
+#pragma unroll
+  for (int p = 0; p < P; ++p) load(p, p);
+  f32x16 acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  auto step = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[slot][i]),
+                                                       __builtin_bit_cast(bf16x8, wr[slot]), acc[i], 0, 0, 0);
+  };
+  // whole rounds of P substeps (a branch-free body, so the loads of one round stay in flight
+  // across the loop edge), then the rem < P substeps left, from the ring as it stands
+  const int rounds = ks_total / P, rem = ks_total - rounds * P;
+  for (int r = 1; r <= rounds; ++r) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      step(p);
+      load(p, r * P + p);
+      __builtin_amdgcn_sched_barrier(0);   // keep each refill right behind the MFMA it follows
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < rem) step(p);
+  // element e of acc[i]: C row m0 + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, column n0 + lane % 32
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (r >= M) continue;
+      const int col = n0 + (lane & 31);
+      if constexpr (OUT_BF16) ((__bf16*)C)[(size_t)r * N + col] = (__bf16)acc[i][e];
+      else ((float*)C)[(size_t)r * N + col] = acc[i][e];
+    }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Products with at most kSkinnyMaxM rows take the skinny kernel: one 32-row tile (ring of 24
+// substeps) up to 32 rows, two (ring of 16) up to 64. Measured on MI355X with K = 4096: the
+// 128 x 128 tiles leave most CUs idle there (N / 128 workgroups), the skinny kernel streams W
+// at 2.9-3.4 TB/s.
+constexpr int kSkinnyMaxM = 64;
+
+template <int TM, int P>
+int launch_skinny(const void* a, const void* w, void* c, int m, int n, int k, int c_dtype, hipStream_t stream) {
+  const dim3 grid((unsigned)(n / 32), (unsigned)((m + 32 * TM - 1) / (32 * TM)));
+  if (c_dtype == 1)
+    hipLaunchKernelGGL((gemm_skinny_kernel<true, TM, P>), grid, dim3(64), 0, stream, (const char*)a,
+                       (const char*)w, (char*)c, m, n, k);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, TM, P>), grid, dim3(64), 0, stream, (const char*)a,
+                       (const char*)w, (char*)c, m, n, k);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 // Large products take 256 x 256 workgroup tiles (one workgroup per CU, 128 x 128 per wave: half
 // the LDS operand reads and half the fabric traffic per flop of the 128 x 128 tile); products
 // with fewer than kBigTilesMin such tiles take 128 x 128 tiles, so the grid still fills the chip.
-// Both walk every element's K in the same 16-wide MFMA steps, so their bits are identical and
-// the choice (which depends on M) cannot make a row's result depend on M.
+// Both walk every element's K in the same 16-wide MFMA steps (as does the skinny kernel for
+// M <= 64), so their bits are identical and the choice, which depends on M, cannot make a row's
+// result depend on M.
 constexpr int kBigTilesMin = 256;
 
 template <int TM, int TN, int BK>
@@ -223,6 +307,8 @@ extern "C" int bi_gemm(const void* a, const void* w, void* c, int32_t m, int32_t
   if ((int64_t)k * 2 * 256 >= ((int64_t)1 << 31)) return 2;   // 32-bit lane offsets inside a tile
   if (m == 0) return 0;
   if (!a || !w || !c || !aligned16(a) || !aligned16(w) || !aligned16(c)) return 1;
+  if (m <= kSkinnyMaxM) return m <= 32 ? launch_skinny<1, 24>(a, w, c, m, n, k, c_dtype, stream)
+                                        : launch_skinny<2, 16>(a, w, c, m, n, k, c_dtype, stream);
   const int64_t big_tiles = (((int64_t)m + 255) / 256) * (n / 256);
   if (n % 256 == 0 && big_tiles >= kBigTilesMin) return launch_gemm<4, 4, 64>(a, w, c, m, n, k, c_dtype, stream);
   return launch_gemm<2, 2, 64>(a, w, c, m, n, k, c_dtype, stream);

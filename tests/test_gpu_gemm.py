@@ -36,8 +36,8 @@ def check(c, a, w, what):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("m,n,k", [(1, 128, 64), (5, 256, 128), (128, 128, 4096), (300, 384, 576),
-                                   (257, 1024, 1024)])
+@pytest.mark.parametrize("m,n,k", [(1, 128, 64), (5, 256, 128), (32, 384, 1024), (33, 256, 576),
+                                   (64, 128, 4096), (128, 128, 4096), (300, 384, 576), (257, 1024, 1024)])
 def test_gemm_parity(out, m, n, k):
     print("CASE gemm", out, m, n, k, flush=True)
     a, w = gemm_inputs(51, m, n, k)
@@ -47,13 +47,14 @@ def test_gemm_parity(out, m, n, k):
 
 
 def test_gemm_rows_are_batch_invariant():
-    """A row's outputs do not depend on M (the token count) or the row's position."""
+    """A row's outputs do not depend on M (the token count) or the row's position: rows computed
+    by the skinny kernel (M <= 64) and by the 128 x 128 tiles are compared with each other."""
     m, n, k = 1000, 512, 2048
     print("CASE gemm invariance", flush=True)
     a, w = gemm_inputs(52, m, n, k)
     ad, wd = torch.from_numpy(a).cuda().to(torch.bfloat16), torch.from_numpy(w).cuda().to(torch.bfloat16)
     full = run(ad, wd)
-    for rows in (1, 3, 127, 128, 129, 600):
+    for rows in (1, 3, 32, 33, 64, 65, 127, 128, 129, 600):
         assert_bitwise(run(ad[:rows].contiguous(), wd), full[:rows], f"first {rows} rows")
     perm = torch.randperm(m, generator=torch.Generator().manual_seed(4)).cuda()
     assert_bitwise(run(ad[perm].contiguous(), wd), full[perm], "permuted rows")
