@@ -73,10 +73,11 @@ def test_gemm_rejects_bad_sizes():
             torch.zeros((128, 96), dtype=torch.bfloat16, device="cuda"))       # K % 64
 
 
-@pytest.mark.parametrize("m,k", [(2048, 256), (2085, 320)])
+@pytest.mark.parametrize("m,k", [(2048, 256), (2085, 320), (1040, 192)])
 def test_gemm_large_tile_parity(m, k):
     """Shapes with at least 256 tiles of 256 x 256 take the large tile (M = 2085: a ragged last
-    tile row; K = 320: an odd number of 64-wide K steps): same bound against the oracle."""
+    tile row; K = 320: an odd number of 64-wide K steps); M = 1040 takes the 128 x 128 tile (too
+    few large tiles, enough 128 x 128 ones): same bound against the oracle."""
     n = 8192
     print("CASE gemm large tile", m, flush=True)
     a, w = gemm_inputs(53, m, n, k)
@@ -87,7 +88,8 @@ def test_gemm_large_tile_parity(m, k):
 
 def test_gemm_rows_same_bits_across_tile_shapes():
     """Rows of a product that takes the 256 x 256 tiles equal, bit for bit, the same rows computed
-    in products small enough to take the 128 x 128 tiles (M = 1, 7, 300)."""
+    in products that take the 128 x 128 tiles (M = 1040), the 64 x 64 tiles (M = 300) and the
+    skinny kernel (M = 1, 7)."""
     m, n, k = 2085, 8192, 512
     print("CASE gemm tile shapes", flush=True)
     a, w = gemm_inputs(54, m, n, k)
@@ -95,6 +97,7 @@ def test_gemm_rows_same_bits_across_tile_shapes():
     for out in (torch.float32, torch.bfloat16):
         full = run(ad, wd, out)
         assert_bitwise(run(ad[:300].contiguous(), wd, out), full[:300], f"first 300 rows {out}")
+        assert_bitwise(run(ad[1000:2040].contiguous(), wd, out), full[1000:2040], f"rows 1000..2039 {out}")
         assert_bitwise(run(ad[2078:].contiguous(), wd, out), full[2078:], f"last 7 rows {out}")
         for r in (0, 1041, 2084):
             assert_bitwise(run(ad[r:r + 1].contiguous(), wd, out), full[r:r + 1], f"row {r} alone {out}")
