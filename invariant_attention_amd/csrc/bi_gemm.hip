@@ -13,12 +13,15 @@
 // register staging; a scalar resource per operand tile and 32-bit lane offsets; the compiler
 // counts them on the vector-memory counter only, so the operand reads wait for just what they
 // need, where a global_load_lds would turn each wait into a wait for every LDS read in flight:
-// 12-18% faster here), two buffers as separate LDS variables, one barrier per K step. LDS rows
+// 12-18% faster here), a ring of 2 to 4 stages (each a separate LDS variable) filled up to
+// stages - 1 K steps ahead, one barrier per K step that waits only for the oldest step. LDS rows
 // are BK bf16; a row's 16-byte chunks are permuted by phys_chunk so that the operand reads (32
 // rows at one chunk) hit distinct banks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "../../include/bi_gemm.h"
 
@@ -30,7 +33,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kKAlign = 64;                      // K must be a multiple of this
 constexpr int kThreadsG = 256;                   // 4 waves in a 2 x 2 grid
-constexpr int kWaitVm0 = 0x0F70;                 // s_waitcnt vmcnt(0)
+// s_waitcnt operands: vmcnt <= n only (expcnt and lgkmcnt at their maximum), and vmcnt <= n
+// with lgkmcnt = 0 (every LDS read of the wave returned)
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int wait_vm_lds0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
 // A wave computes TM x TN MFMA tiles of 32 x 32 (rows x columns of C); the workgroup tile is
 // BM x BN = 64 TM x 64 TN, staged BK columns of K at a time. Neither the tile shape nor BK
 // changes any element's order of products (16-wide MFMA k-substeps, ascending).
@@ -41,6 +47,14 @@ template <int TM, int TN, int BK_> struct GemmTile {
   static constexpr int A_ROUNDS = BM * CPR / kThreadsG, W_ROUNDS = BN * CPR / kThreadsG;
 };
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in that order
+template <int N, int J = 0, class F> __device__ __forceinline__ void for_stages(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>{});
+    for_stages<N, J + 1>(f);
+  }
+}
+
 // Chunk c of LDS row R is stored at chunk phys_chunk(c, R): the 16 rows that one pass of a
 // 16-byte operand read touches (one chunk each) then fall on 16 distinct 16-byte bank groups.
 template <int CPR> __device__ __forceinline__ int phys_chunk(int c, int row) {
@@ -48,15 +62,36 @@ template <int CPR> __device__ __forceinline__ int phys_chunk(int c, int row) {
   else return c ^ ((row >> 2) & 3);
 }
 
-template <bool OUT_BF16, int TM, int TN, int BK, int MINB>
+template <bool OUT_BF16, int TM, int TN, int BK, int NS, int MINB>
 __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, const char* W, char* C, int M,
                                                               int N, int K) {
   using T = GemmTile<TM, TN, BK>;
   constexpr int BM = T::BM, BN = T::BN, CPR = T::CPR, KS = BK / 16;
-  __shared__ __attribute__((aligned(16))) char a0[T::A_BYTES];   // even K steps
-  __shared__ __attribute__((aligned(16))) char w0[T::W_BYTES];
-  __shared__ __attribute__((aligned(16))) char a1[T::A_BYTES];   // odd K steps
-  __shared__ __attribute__((aligned(16))) char w1[T::W_BYTES];
+  // NS stages: K step kt lives in stage kt % NS. Each stage is a variable of its own, so the
+  // compiler can tell that the reads of one stage do not wait for the transfers into another.
+  static_assert(NS >= 2 && NS <= 8, "stages");
+#define BI_GEMM_STAGE(i)                                                                     \
+  __shared__ __attribute__((aligned(16))) char sa##i[NS > i ? T::A_BYTES : 16];               \
+  __shared__ __attribute__((aligned(16))) char sw##i[NS > i ? T::W_BYTES : 16];
+  BI_GEMM_STAGE(0) BI_GEMM_STAGE(1) BI_GEMM_STAGE(2) BI_GEMM_STAGE(3)
+  BI_GEMM_STAGE(4) BI_GEMM_STAGE(5) BI_GEMM_STAGE(6) BI_GEMM_STAGE(7)
+#undef BI_GEMM_STAGE
+  // stage J's buffers, named directly (no pointer table, so every access keeps its LDS address
+  // space and its variable)
+  auto stage_a = [&](auto J) __attribute__((always_inline)) -> char* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return sa0; else if constexpr (j == 1) return sa1;
+    else if constexpr (j == 2) return sa2; else if constexpr (j == 3) return sa3;
+    else if constexpr (j == 4) return sa4; else if constexpr (j == 5) return sa5;
+    else if constexpr (j == 6) return sa6; else return sa7;
+  };
+  auto stage_w = [&](auto J) __attribute__((always_inline)) -> char* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return sw0; else if constexpr (j == 1) return sw1;
+    else if constexpr (j == 2) return sw2; else if constexpr (j == 3) return sw3;
+    else if constexpr (j == 4) return sw4; else if constexpr (j == 5) return sw5;
+    else if constexpr (j == 6) return sw6; else return sw7;
+  };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int ntn = N / BN;
@@ -153,22 +188,40 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
     }
   };
 
+  // Step kt: wait for this wave's transfers of step kt (the later NS - 2 steps' may still be in
+  // flight), barrier (every wave's transfers of step kt have landed, and every wave is done with
+  // step kt - 1), refill the stage of step kt - 1 with step kt + NS - 1, compute step kt.
+  // Transfers past the last step re-load it into stages that are not read again, so every step
+  // issues the same number of transfers and the wait count is the same constant throughout.
+  constexpr int R = T::A_ROUNDS + T::W_ROUNDS;   // transfers per step per wave
   const int KT = K / BK;
-  dma(0, a0, w0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  // pairs of K steps (one loop exit, so the accumulators stay in place), then an odd last step
-  for (int kt = 0; kt + 1 < KT; kt += 2) {
-    dma(kt + 1, a1, w1);
-    compute(a0, w0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (kt + 2 < KT) dma(kt + 2, a0, w0);
-    compute(a1, w1);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-  }
-  if (KT & 1) compute(a0, w0);
+  for_stages<NS - 1>([&](auto J) __attribute__((always_inline)) {
+    dma(min((int)decltype(J)::value, KT - 1), stage_a(J), stage_w(J));
+  });
+  auto body = [&](int kt, auto J) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
+    using Jn = std::integral_constant<int, (j + NS - 1) % NS>;
+    // A plain barrier, not __syncthreads(): its release fence would wait for every transfer in
+    // flight. None is needed here: LDS has no cache, a wave's transfers are in LDS once its
+    // vmcnt has dropped, and lgkmcnt = 0 means every LDS read of the wave (those of the stage
+    // refilled below included) has returned before it reaches the barrier. The empty asm
+    // keeps the compiler from moving memory accesses across the barrier.
+    __builtin_amdgcn_s_waitcnt(wait_vm_lds0((NS - 2) * R));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    dma(min(kt + NS - 1, KT - 1), stage_a(Jn{}), stage_w(Jn{}));
+    compute(stage_a(J), stage_w(J));
+  };
+  // whole rounds of NS steps (one loop exit, so the accumulators stay in place), then the rest
+  const int rounds = KT / NS, rest = KT - rounds * NS;
+  for (int r = 0; r < rounds; ++r)
+    for_stages<NS>([&](auto J) __attribute__((always_inline)) { body(r * NS + decltype(J)::value, J); });
+  for_stages<NS>([&](auto J) __attribute__((always_inline)) {
+    if (decltype(J)::value < rest) body(rounds * NS + decltype(J)::value, J);
+  });
+  // the transfers past the last step must land before the workgroup's LDS can be handed on
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // epilogue: element e of acc[i][j] is C row (BM / 2) wm + 32 i + 8 (e / 4) + 4 (lane / 32) +
   // e % 4, column (BN / 2) wn + 32 j + lane % 32
@@ -280,22 +333,26 @@ int launch_skinny(const void* a, const void* w, void* c, int m, int n, int k, in
 // M <= 64), so their bits are identical and the choice, which depends on M, cannot make a row's
 // result depend on M.
 constexpr int kBigTilesMin = 256;
+// LDS stages per tile shape (64-wide K steps): 256 x 256 tiles 2 (128 KB), 128 x 128 tiles 2
+// (64 KB, two workgroups per CU), 64 x 64 tiles 4 (64 KB): measured on MI355X, more stages (or
+// 32-wide K steps with more stages) gained nothing for the larger tiles, and cut the 64 x 64
+// tiles' time by half or more.
 // Products with fewer than kMidTilesMax tiles of 128 x 128 (M from 65 to a few hundred) take
 // 64 x 64 tiles (32 x 32 per wave): four times the workgroups; 20-35% faster there on MI355X.
 constexpr int kMidTilesMax = 256;
 
-template <int TM, int TN, int BK>
+template <int TM, int TN, int BK, int NS>
 int launch_gemm(const void* a, const void* w, void* c, int m, int n, int k, int c_dtype, hipStream_t stream) {
   using T = GemmTile<TM, TN, BK>;
-  constexpr int MINB = (2 * (T::A_BYTES + T::W_BYTES) <= 80 * 1024) ? 2 : 1;
+  constexpr int MINB = (NS * (T::A_BYTES + T::W_BYTES) <= 80 * 1024) ? 2 : 1;
   if (n % T::BN) return 2;
   const int64_t tiles = (((int64_t)m + T::BM - 1) / T::BM) * (n / T::BN);
   if (tiles > 0x7fffffff) return 2;
   if (c_dtype == 1)
-    hipLaunchKernelGGL((gemm_kernel<true, TM, TN, BK, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<true, TM, TN, BK, NS, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
                        (const char*)a, (const char*)w, (char*)c, m, n, k);
   else
-    hipLaunchKernelGGL((gemm_kernel<false, TM, TN, BK, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<false, TM, TN, BK, NS, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
                        (const char*)a, (const char*)w, (char*)c, m, n, k);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
@@ -313,8 +370,8 @@ extern "C" int bi_gemm(const void* a, const void* w, void* c, int32_t m, int32_t
   if (m <= kSkinnyMaxM) return m <= 32 ? launch_skinny<1, 24>(a, w, c, m, n, k, c_dtype, stream)
                                         : launch_skinny<2, 16>(a, w, c, m, n, k, c_dtype, stream);
   const int64_t big_tiles = (((int64_t)m + 255) / 256) * (n / 256);
-  if (n % 256 == 0 && big_tiles >= kBigTilesMin) return launch_gemm<4, 4, 64>(a, w, c, m, n, k, c_dtype, stream);
+  if (n % 256 == 0 && big_tiles >= kBigTilesMin) return launch_gemm<4, 4, 64, 2>(a, w, c, m, n, k, c_dtype, stream);
   const int64_t tiles128 = (((int64_t)m + 127) / 128) * (n / 128);
-  if (tiles128 < kMidTilesMax) return launch_gemm<1, 1, 64>(a, w, c, m, n, k, c_dtype, stream);
-  return launch_gemm<2, 2, 64>(a, w, c, m, n, k, c_dtype, stream);
+  if (tiles128 < kMidTilesMax) return launch_gemm<1, 1, 64, 4>(a, w, c, m, n, k, c_dtype, stream);
+  return launch_gemm<2, 2, 64, 2>(a, w, c, m, n, k, c_dtype, stream);
 }

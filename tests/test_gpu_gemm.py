@@ -37,7 +37,8 @@ def check(c, a, w, what):
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (5, 256, 128), (32, 384, 1024), (33, 256, 576),
-                                   (64, 128, 4096), (128, 128, 4096), (300, 384, 576), (257, 1024, 1024)])
+                                   (64, 128, 4096), (100, 128, 64), (100, 256, 192), (128, 128, 4096),
+                                   (300, 384, 576), (257, 1024, 1024)])
 def test_gemm_parity(out, m, n, k):
     print("CASE gemm", out, m, n, k, flush=True)
     a, w = gemm_inputs(51, m, n, k)
