@@ -308,11 +308,11 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(const char* A, const ch
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Products with at most kSkinnyMaxM rows take the skinny kernel: one 32-row tile (ring of 24
-// substeps) up to 32 rows, two (ring of 16) up to 64. Measured on MI355X with K = 4096: the
-// 128 x 128 tiles leave most CUs idle there (N / 128 workgroups), the skinny kernel streams W
-// at 2.9-3.4 TB/s.
-constexpr int kSkinnyMaxM = 64;
+// Products with at most kSkinnyMaxM rows and a K of at least kSkinnyMinK take the skinny kernel
+// (one 32-row tile, a ring of 24 substeps): there it has twice the workgroups of the 64 x 64
+// tiles (N / 32) and streams W 1.0-1.4x faster than they do on MI355X (M = 1 to 16, K = 8192
+// and 14336); at K = 4096 the staged 64 x 64 tiles are as fast or faster.
+constexpr int kSkinnyMaxM = 16, kSkinnyMinK = 8192;
 
 template <int TM, int P>
 int launch_skinny(const void* a, const void* w, void* c, int m, int n, int k, int c_dtype, hipStream_t stream) {
@@ -329,9 +329,9 @@ int launch_skinny(const void* a, const void* w, void* c, int m, int n, int k, in
 // Large products take 256 x 256 workgroup tiles (one workgroup per CU, 128 x 128 per wave: half
 // the LDS operand reads and half the fabric traffic per flop of the 128 x 128 tile); products
 // with fewer than kBigTilesMin such tiles take 128 x 128 tiles, so the grid still fills the chip.
-// Both walk every element's K in the same 16-wide MFMA steps (as does the skinny kernel for
-// M <= 64), so their bits are identical and the choice, which depends on M, cannot make a row's
-// result depend on M.
+// Both walk every element's K in the same 16-wide MFMA steps (as do the 64 x 64 tiles and the
+// skinny kernel), so their bits are identical and the choice, which depends on M, cannot make a
+// row's result depend on M.
 constexpr int kBigTilesMin = 256;
 // LDS stages per tile shape (64-wide K steps): 256 x 256 tiles 2 (128 KB), 128 x 128 tiles 2
 // (64 KB, two workgroups per CU), 64 x 64 tiles 4 (64 KB): measured on MI355X, more stages (or
@@ -367,8 +367,7 @@ extern "C" int bi_gemm(const void* a, const void* w, void* c, int32_t m, int32_t
   if ((int64_t)k * 2 * 256 >= ((int64_t)1 << 31)) return 2;   // 32-bit lane offsets inside a tile
   if (m == 0) return 0;
   if (!a || !w || !c || !aligned16(a) || !aligned16(w) || !aligned16(c)) return 1;
-  if (m <= kSkinnyMaxM) return m <= 32 ? launch_skinny<1, 24>(a, w, c, m, n, k, c_dtype, stream)
-                                        : launch_skinny<2, 16>(a, w, c, m, n, k, c_dtype, stream);
+  if (m <= kSkinnyMaxM && k >= kSkinnyMinK) return launch_skinny<1, 24>(a, w, c, m, n, k, c_dtype, stream);
   const int64_t big_tiles = (((int64_t)m + 255) / 256) * (n / 256);
   if (n % 256 == 0 && big_tiles >= kBigTilesMin) return launch_gemm<4, 4, 64, 2>(a, w, c, m, n, k, c_dtype, stream);
   const int64_t tiles128 = (((int64_t)m + 127) / 128) * (n / 128);

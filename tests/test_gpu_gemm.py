@@ -38,7 +38,7 @@ def check(c, a, w, what):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (5, 256, 128), (32, 384, 1024), (33, 256, 576),
                                    (64, 128, 4096), (100, 128, 64), (100, 256, 192), (128, 128, 4096),
-                                   (300, 384, 576), (257, 1024, 1024)])
+                                   (300, 384, 576), (257, 1024, 1024), (1, 128, 8192), (16, 256, 8256)])
 def test_gemm_parity(out, m, n, k):
     print("CASE gemm", out, m, n, k, flush=True)
     a, w = gemm_inputs(51, m, n, k)
@@ -63,6 +63,19 @@ def test_gemm_rows_are_batch_invariant():
         assert_bitwise(run(ad[r:r + 1].contiguous(), wd), full[r:r + 1], f"row {r} alone")
     fb = run(ad, wd, torch.bfloat16)
     assert_bitwise(run(ad[7:8].contiguous(), wd, torch.bfloat16), fb[7:8], "bf16 output row")
+
+
+def test_gemm_skinny_rows_same_bits():
+    """With K >= 8192, up to 16 rows take the skinny kernel (operands straight from memory, no
+    LDS); its rows equal, bit for bit, the same rows of a 300-row product (64 x 64 tiles)."""
+    m, n, k = 300, 256, 8256
+    print("CASE gemm skinny invariance", flush=True)
+    a, w = gemm_inputs(55, m, n, k)
+    ad, wd = torch.from_numpy(a).cuda().to(torch.bfloat16), torch.from_numpy(w).cuda().to(torch.bfloat16)
+    for out in (torch.float32, torch.bfloat16):
+        full = run(ad, wd, out)
+        for lo, hi in ((0, 16), (0, 17), (150, 151), (284, 300)):
+            assert_bitwise(run(ad[lo:hi].contiguous(), wd, out), full[lo:hi], f"rows {lo}..{hi - 1} {out}")
 
 
 def test_gemm_rejects_bad_sizes():
