@@ -438,6 +438,19 @@ def run_gemm_bench(args, result):
     ms_v = timed(lambda: torch.matmul(a, w.t(), out=c), n_it)
     fl = 2.0 * m * n * k
     tf, tf_v = fl / (ms * 1e-3) / 1e12, fl / (ms_v * 1e-3) / 1e12
+    # token counts of decode and small prefill chunks (other kernels: 64 x 64 tiles, skinny);
+    # W rotated over four copies so it is not cache resident, bandwidth of W
+    small = {}
+    for sm, sn, sk in ((1, 4096, 4096), (64, 8192, 4096), (128, 14336, 4096), (1, 8192, 14336)):
+        sa = torch.randn((sm, sk), device="cuda", generator=g).to(torch.bfloat16)
+        sws = [(torch.randn((sn, sk), device="cuda", generator=g) / 64).to(torch.bfloat16) for _ in range(4)]
+        sc = torch.empty((sm, sn), device="cuda", dtype=torch.bfloat16)
+        it = iter(range(1 << 30))
+        t_b = timed(lambda: bi.bi_gemm(sa, sws[next(it) % 4], sc), 20)
+        t_v = timed(lambda: torch.matmul(sa, sws[next(it) % 4].t(), out=sc), 20)
+        small[f"{sm}x{sn}x{sk}"] = {"us": t_b * 1e3, "w_gbs": sn * sk * 2 / (t_b * 1e-3) / 1e9,
+                                    "hipblaslt_us": t_v * 1e3, "ratio": t_v / t_b}
+        del sa, sws, sc
     result["gemm"] = {"value": tf, "unit": "TFLOP/s", "ms": ms,
                       "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
@@ -446,10 +459,12 @@ def run_gemm_bench(args, result):
                       "vs_hipblaslt": {"hipblaslt_tflops": tf_v, "ratio": tf / tf_v,
                                        "hipblaslt_rows_same_bits_at_m1": vendor_same},
                       "bits": "rows 0, 4097, 8191 at M = 1 equal to the M = 8192 call",
+                      "small_m": small,
                       "config": {"workload": "gemm_bf16: C[8192][8192] = A[8192][4096] W[8192][4096]^T, "
                                              "bf16 in and out, fp32 accumulation"}}
     log(f"gemm: {tf:.0f} TFLOP/s ({tf / tf_v:.2f}x hipBLASLt {tf_v:.0f}; hipBLASLt rows same bits "
-        f"at M = 1: {vendor_same})")
+        f"at M = 1: {vendor_same}); small M: " +
+        ", ".join(f"{kk} {v['us']:.1f} us ({v['ratio']:.2f}x)" for kk, v in small.items()))
 
 
 # ----------------------------------------------------------------------------- CPU baseline
