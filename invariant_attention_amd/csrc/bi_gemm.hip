@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
   const size_t rowb = (size_t)K * 2;               // bytes per row of A and W
 
   // DMA: slot p = 256 t + 64 wave + lane of a tile is LDS row p / CPR, physical chunk p % CPR,
-  // which holds the logical chunk that phys_chunk maps there (phys_chunk is an involution). Rows of A past M read row M - 1
-  // (their outputs are not written).
+  // which holds the logical chunk that phys_chunk maps there (phys_chunk is an involution).
+  // Rows of A past M read row M - 1 (their outputs are not written).
   unsigned a_vo[T::A_ROUNDS], w_vo[T::W_ROUNDS];
 #pragma unroll
   for (int t = 0; t < T::A_ROUNDS; ++t) {
