@@ -32,7 +32,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kKAlign = 64;                      // K must be a multiple of this
-constexpr int kThreadsG = 256;                   // 4 waves in a 2 x 2 grid
+// NWV waves per workgroup (4 or 8) in a 2 x NWV / 2 grid
 // s_waitcnt operands: vmcnt <= n only (expcnt and lgkmcnt at their maximum), and vmcnt <= n
 // with lgkmcnt = 0 (every LDS read of the wave returned)
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
@@ -40,11 +40,13 @@ constexpr int wait_vm_lds0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14);
 // A wave computes TM x TN MFMA tiles of 32 x 32 (rows x columns of C); the workgroup tile is
 // BM x BN = 64 TM x 64 TN, staged BK columns of K at a time. Neither the tile shape nor BK
 // changes any element's order of products (16-wide MFMA k-substeps, ascending).
-template <int TM, int TN, int BK_> struct GemmTile {
+template <int TM, int TN, int BK_, int NWV_ = 4> struct GemmTile {
   static constexpr int BK = BK_, CPR = BK / 8;   // 16-byte chunks per LDS row
-  static constexpr int BM = 64 * TM, BN = 64 * TN;
+  static constexpr int NWV = NWV_, NT = 64 * NWV, WGN = NWV / 2;
+  static constexpr int BM = 64 * TM, BN = 32 * TN * WGN;
   static constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2;
-  static constexpr int A_ROUNDS = BM * CPR / kThreadsG, W_ROUNDS = BN * CPR / kThreadsG;
+  static constexpr int A_ROUNDS = BM * CPR / NT, W_ROUNDS = BN * CPR / NT;
+  static_assert(A_ROUNDS * NT == BM * CPR && W_ROUNDS * NT == BN * CPR, "tile vs threads");
 };
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in that order
@@ -62,10 +64,11 @@ template <int CPR> __device__ __forceinline__ int phys_chunk(int c, int row) {
   else return c ^ ((row >> 2) & 3);
 }
 
-template <bool OUT_BF16, int TM, int TN, int BK, int NS, int MINB>
-__global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, const char* W, char* C, int M,
+template <bool OUT_BF16, int TM, int TN, int BK, int NS, int NWV, int MINB>
+__global__ __launch_bounds__(64 * NWV, MINB) void gemm_kernel(const char* A, const char* W, char* C, int M,
                                                               int N, int K) {
-  using T = GemmTile<TM, TN, BK>;
+  using T = GemmTile<TM, TN, BK, NWV>;
+  constexpr int NT = T::NT, WGN = T::WGN;
   constexpr int BM = T::BM, BN = T::BN, CPR = T::CPR, KS = BK / 16;
   // NS stages: K step kt lives in stage kt % NS. Each stage is a variable of its own, so the
   // compiler can tell that the reads of one stage do not wait for the transfers into another.
@@ -99,18 +102,18 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
   const int m0 = tm * BM, n0 = tn * BN;
   const size_t rowb = (size_t)K * 2;               // bytes per row of A and W
 
-  // DMA: slot p = 256 t + 64 wave + lane of a tile is LDS row p / CPR, physical chunk p % CPR,
+  // DMA: slot p = NT t + 64 wave + lane of a tile is LDS row p / CPR, physical chunk p % CPR,
   // which holds the logical chunk that phys_chunk maps there (phys_chunk is an involution).
   // Rows of A past M read row M - 1 (their outputs are not written).
   unsigned a_vo[T::A_ROUNDS], w_vo[T::W_ROUNDS];
 #pragma unroll
   for (int t = 0; t < T::A_ROUNDS; ++t) {
-    const int p = 256 * t + 64 * wave + lane, R = p / CPR;
+    const int p = NT * t + 64 * wave + lane, R = p / CPR;
     a_vo[t] = (unsigned)((min(m0 + R, M - 1) - m0) * rowb) + phys_chunk<CPR>(p % CPR, R) * 16;
   }
 #pragma unroll
   for (int t = 0; t < T::W_ROUNDS; ++t) {
-    const int p = 256 * t + 64 * wave + lane, R = p / CPR;
+    const int p = NT * t + 64 * wave + lane, R = p / CPR;
     w_vo[t] = (unsigned)(R * rowb) + phys_chunk<CPR>(p % CPR, R) * 16;
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -124,14 +127,14 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
     const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), (short)0, 0x7fffffff, 0x00020000);
 #pragma unroll
     for (int t = 0; t < T::A_ROUNDS; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)&da[(256 * t + 64 * wave) * 16], 16, a_vo[t] + kb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)&da[(NT * t + 64 * wave) * 16], 16, a_vo[t] + kb, 0, 0, 0);
 #pragma unroll
     for (int t = 0; t < T::W_ROUNDS; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)&dw[(256 * t + 64 * wave) * 16], 16, w_vo[t] + kb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)&dw[(NT * t + 64 * wave) * 16], 16, w_vo[t] + kb, 0, 0, 0);
 #endif
   };
 
-  // operand reads: A rows (BM / 2) wm + 32 i + lane % 32, W rows (BN / 2) wn + 32 j + lane % 32,
+  // operand reads: A rows (BM / 2) wm + 32 i + lane % 32, W rows (BN / WGN) wn + 32 j + lane % 32,
   // logical chunk 2 ks + lane / 32 (k = 16 ks + 8 (lane / 32) .. + 7)
   const int wm = wave & 1, wn = wave >> 1;
   unsigned rd_a[TM][KS], rd_w[TN][KS];
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int rw = (BN / 2) * wn + 32 * j + (lane & 31);
+      const int rw = (BN / WGN) * wn + 32 * j + (lane & 31);
       rd_w[j][ks] = (unsigned)(rw * BK * 2 + phys_chunk<CPR>(c, rw) * 16);
     }
   }
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // epilogue: element e of acc[i][j] is C row (BM / 2) wm + 32 i + 8 (e / 4) + 4 (lane / 32) +
-  // e % 4, column (BN / 2) wn + 32 j + lane % 32
+  // e % 4, column (BN / WGN) wn + 32 j + lane % 32
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(kThreadsG, MINB) void gemm_kernel(const char* A, co
       if (r >= M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = n0 + (BN / 2) * wn + 32 * j + (lane & 31);
+        const int col = n0 + (BN / WGN) * wn + 32 * j + (lane & 31);
         const float v = acc[i][j][e];
         if constexpr (OUT_BF16) ((__bf16*)C)[(size_t)r * N + col] = (__bf16)v;
         else ((float*)C)[(size_t)r * N + col] = v;
@@ -326,13 +329,16 @@ int launch_skinny(const void* a, const void* w, void* c, int m, int n, int k, in
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
-// Large products take 256 x 256 workgroup tiles (one workgroup per CU, 128 x 128 per wave: half
-// the LDS operand reads and half the fabric traffic per flop of the 128 x 128 tile); products
+// Large products take 256 x 256 workgroup tiles (one workgroup of 8 waves per CU, 128 x 64 per
+// wave, two waves per SIMD so that one's barrier and transfer waits overlap the other's MFMAs:
+// 6-10% faster than 4 waves of 128 x 128 on MI355X; half the fabric traffic per flop of the
+// 128 x 128 tile, which keeps 4 waves: 8 measured 2-3% slower there); products
 // with fewer than kBigTilesMin such tiles take 128 x 128 tiles, so the grid still fills the chip.
 // Both walk every element's K in the same 16-wide MFMA steps (as do the 64 x 64 tiles and the
 // skinny kernel), so their bits are identical and the choice, which depends on M, cannot make a
 // row's result depend on M.
 constexpr int kBigTilesMin = 256;
+
 // LDS stages per tile shape (64-wide K steps): 256 x 256 tiles 2 (128 KB), 128 x 128 tiles 2
 // (64 KB, two workgroups per CU), 64 x 64 tiles 4 (64 KB): measured on MI355X, more stages (or
 // 32-wide K steps with more stages) gained nothing for the larger tiles, and cut the 64 x 64
@@ -341,18 +347,18 @@ constexpr int kBigTilesMin = 256;
 // 64 x 64 tiles (32 x 32 per wave): four times the workgroups; 20-35% faster there on MI355X.
 constexpr int kMidTilesMax = 256;
 
-template <int TM, int TN, int BK, int NS>
+template <int TM, int TN, int BK, int NS, int NWV = 4>
 int launch_gemm(const void* a, const void* w, void* c, int m, int n, int k, int c_dtype, hipStream_t stream) {
-  using T = GemmTile<TM, TN, BK>;
+  using T = GemmTile<TM, TN, BK, NWV>;
   constexpr int MINB = (NS * (T::A_BYTES + T::W_BYTES) <= 80 * 1024) ? 2 : 1;
   if (n % T::BN) return 2;
   const int64_t tiles = (((int64_t)m + T::BM - 1) / T::BM) * (n / T::BN);
   if (tiles > 0x7fffffff) return 2;
   if (c_dtype == 1)
-    hipLaunchKernelGGL((gemm_kernel<true, TM, TN, BK, NS, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<true, TM, TN, BK, NS, NWV, MINB>), dim3((unsigned)tiles), dim3(T::NT), 0, stream,
                        (const char*)a, (const char*)w, (char*)c, m, n, k);
   else
-    hipLaunchKernelGGL((gemm_kernel<false, TM, TN, BK, NS, MINB>), dim3((unsigned)tiles), dim3(kThreadsG), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<false, TM, TN, BK, NS, NWV, MINB>), dim3((unsigned)tiles), dim3(T::NT), 0, stream,
                        (const char*)a, (const char*)w, (char*)c, m, n, k);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
@@ -369,8 +375,8 @@ extern "C" int bi_gemm(const void* a, const void* w, void* c, int32_t m, int32_t
   if (!a || !w || !c || !aligned16(a) || !aligned16(w) || !aligned16(c)) return 1;
   if (m <= kSkinnyMaxM && k >= kSkinnyMinK) return launch_skinny<1, 24>(a, w, c, m, n, k, c_dtype, stream);
   const int64_t big_tiles = (((int64_t)m + 255) / 256) * (n / 256);
-  if (n % 256 == 0 && big_tiles >= kBigTilesMin) return launch_gemm<4, 4, 64, 2>(a, w, c, m, n, k, c_dtype, stream);
+  if (n % 256 == 0 && big_tiles >= kBigTilesMin) return launch_gemm<4, 2, 64, 2, 8>(a, w, c, m, n, k, c_dtype, stream);
   const int64_t tiles128 = (((int64_t)m + 127) / 128) * (n / 128);
   if (tiles128 < kMidTilesMax) return launch_gemm<1, 1, 64, 4>(a, w, c, m, n, k, c_dtype, stream);
-  return launch_gemm<2, 2, 64, 2>(a, w, c, m, n, k, c_dtype, stream);
+  return launch_gemm<2, 2, 64, 2, 4>(a, w, c, m, n, k, c_dtype, stream);
 }
