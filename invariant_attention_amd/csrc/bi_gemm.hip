@@ -1,6 +1,6 @@
-// bi_gemm.hip — batch-invariant GEMM C = A W^T (gfx950): fixed output tiles (128 x 128, or
-// 256 x 256 for large products), the whole of K inside one workgroup in ascending order, MFMA
-// 32x32x16 bf16.
+// bi_gemm.hip — batch-invariant GEMM C = A W^T (gfx950): output tiles of 256 x 256, 128 x 128
+// or 64 x 64 (or 32 x 32 per wave for few rows and long K), the whole of K inside one workgroup
+// in ascending order, MFMA 32x32x16 bf16.
 //
 // The matmul is made batch invariant by a fixed tile configuration with no Split-K (xitu-tech.com
 // report, section 构建确定性解决方案, matrix multiplication item): the output is cut into 2-D tiles
@@ -32,14 +32,14 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kKAlign = 64;                      // K must be a multiple of this
-// NWV waves per workgroup (4 or 8) in a 2 x NWV / 2 grid
 // s_waitcnt operands: vmcnt <= n only (expcnt and lgkmcnt at their maximum), and vmcnt <= n
 // with lgkmcnt = 0 (every LDS read of the wave returned)
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int wait_vm_lds0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
-// A wave computes TM x TN MFMA tiles of 32 x 32 (rows x columns of C); the workgroup tile is
-// BM x BN = 64 TM x 64 TN, staged BK columns of K at a time. Neither the tile shape nor BK
-// changes any element's order of products (16-wide MFMA k-substeps, ascending).
+// A wave computes TM x TN MFMA tiles of 32 x 32 (rows x columns of C); NWV waves (4 or 8) form a
+// 2 x NWV / 2 grid, so the workgroup tile is BM x BN = 64 TM x 16 TN NWV, staged BK columns of K
+// at a time. Neither the tile shape, the wave count nor BK changes any element's order of
+// products (16-wide MFMA k-substeps, ascending).
 template <int TM, int TN, int BK_, int NWV_ = 4> struct GemmTile {
   static constexpr int BK = BK_, CPR = BK / 8;   // 16-byte chunks per LDS row
   static constexpr int NWV = NWV_, NT = 64 * NWV, WGN = NWV / 2;
