@@ -24,7 +24,7 @@ extern "C" {
  * C[M][N] = A[M][K] W[N][K]^T (a linear layer: activations times the transpose of an
  * [out][in] weight), bf16 inputs, fp32 accumulation. One workgroup owns a tile of C (M <= 16
  * and K >= 8192: 32 rows x 32 columns, one wave, operands straight from memory; else 256 x 256
- * when there are at least 256 such tiles and N is a multiple of 256; else 128 x 128, or 64 x 64
+ * when there are at least 160 such tiles and N is a multiple of 256; else 128 x 128, or 64 x 64
  * when there would be fewer than 256 tiles of 128 x 128) and walks the
  * whole of K as MFMA 32x32x16 k-substeps in ascending order into one fp32 accumulator per
  * element: no split of K, and the same per-element order for every M and every tile shape,

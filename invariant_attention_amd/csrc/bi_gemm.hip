@@ -333,11 +333,13 @@ int launch_skinny(const void* a, const void* w, void* c, int m, int n, int k, in
 // wave, two waves per SIMD so that one's barrier and transfer waits overlap the other's MFMAs:
 // 6-10% faster than 4 waves of 128 x 128 on MI355X; half the fabric traffic per flop of the
 // 128 x 128 tile, which keeps 4 waves: 8 measured 2-3% slower there); products
-// with fewer than kBigTilesMin such tiles take 128 x 128 tiles, so the grid still fills the chip.
+// with fewer than kBigTilesMin such tiles take 128 x 128 tiles, so the grid still fills the chip
+// (160 rather than 256, one per CU: 7-15% faster on MI355X for shapes with 160 to 255 large tiles,
+// e.g. 1536 x 8192, 3072 x 4096, whose 128 x 128 tiles would run a second, partial round).
 // Both walk every element's K in the same 16-wide MFMA steps (as do the 64 x 64 tiles and the
 // skinny kernel), so their bits are identical and the choice, which depends on M, cannot make a
 // row's result depend on M.
-constexpr int kBigTilesMin = 256;
+constexpr int kBigTilesMin = 160;
 
 // LDS stages per tile shape (64-wide K steps): 256 x 256 tiles 2 (128 KB), 128 x 128 tiles 2
 // (64 KB, two workgroups per CU), 64 x 64 tiles 4 (64 KB): measured on MI355X, more stages (or

@@ -87,12 +87,12 @@ def test_gemm_rejects_bad_sizes():
             torch.zeros((128, 96), dtype=torch.bfloat16, device="cuda"))       # K % 64
 
 
-@pytest.mark.parametrize("m,k", [(2048, 256), (2085, 320), (1040, 192)])
-def test_gemm_large_tile_parity(m, k):
-    """Shapes with at least 256 tiles of 256 x 256 take the large tile (M = 2085: a ragged last
-    tile row; K = 320: an odd number of 64-wide K steps); M = 1040 takes the 128 x 128 tile (too
-    few large tiles, enough 128 x 128 ones): same bound against the oracle."""
-    n = 8192
+@pytest.mark.parametrize("m,n,k", [(2048, 8192, 256), (2085, 8192, 320), (1040, 8192, 192),
+                                   (1040, 4224, 192)])
+def test_gemm_large_tile_parity(m, n, k):
+    """Shapes with at least 160 tiles of 256 x 256 take the large tile (M = 2085: a ragged last
+    tile row; K = 320 and 192: an odd number of 64-wide K steps); N = 4224 (not a multiple of 256)
+    takes the 128 x 128 tile: same bound against the oracle."""
     print("CASE gemm large tile", m, flush=True)
     a, w = gemm_inputs(53, m, n, k)
     ad, wd = torch.from_numpy(a).cuda().to(torch.bfloat16), torch.from_numpy(w).cuda().to(torch.bfloat16)
@@ -102,8 +102,8 @@ def test_gemm_large_tile_parity(m, k):
 
 def test_gemm_rows_same_bits_across_tile_shapes():
     """Rows of a product that takes the 256 x 256 tiles equal, bit for bit, the same rows computed
-    in products that take the 128 x 128 tiles (M = 1040), the 64 x 64 tiles (M = 300) and the
-    skinny kernel (M = 1, 7)."""
+    in products that take the 128 x 128 tiles (M = 600), the 64 x 64 tiles (M = 300) and the
+    64 x 64 tiles at M = 1, 7 (K = 512: below the skinny kernel's K)."""
     m, n, k = 2085, 8192, 512
     print("CASE gemm tile shapes", flush=True)
     a, w = gemm_inputs(54, m, n, k)
@@ -111,7 +111,7 @@ def test_gemm_rows_same_bits_across_tile_shapes():
     for out in (torch.float32, torch.bfloat16):
         full = run(ad, wd, out)
         assert_bitwise(run(ad[:300].contiguous(), wd, out), full[:300], f"first 300 rows {out}")
-        assert_bitwise(run(ad[1000:2040].contiguous(), wd, out), full[1000:2040], f"rows 1000..2039 {out}")
+        assert_bitwise(run(ad[1000:1600].contiguous(), wd, out), full[1000:1600], f"rows 1000..1599 {out}")
         assert_bitwise(run(ad[2078:].contiguous(), wd, out), full[2078:], f"last 7 rows {out}")
         for r in (0, 1041, 2084):
             assert_bitwise(run(ad[r:r + 1].contiguous(), wd, out), full[r:r + 1], f"row {r} alone {out}")
