@@ -325,8 +325,7 @@ def run_prefill_bench(args, result):
                                   "traffic": profiled_traffic("prefill_kernel")}
     result["variant_slowdown"]["prefill"] = kern / kern_v - 1.0 if kern_v else None
     result["variant_slowdown"]["prefill_ms"] = {"invariant": kern, "split_by_batch": kern_v}
-    if not args.profile_run:
-        run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref)
+    run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref)
     return bt, ref
 
 
@@ -358,8 +357,13 @@ def run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref):
     tm.mark(1)
     torch.cuda.synchronize()
     ms = tm.ms(0, 1) / n
-    result["varlen"] = {"kernel_tflops": prefill_flops(bt) / (ms * 1e-3) / 1e12, "kernel_ms": ms,
+    tf = prefill_flops(bt) / (ms * 1e-3) / 1e12
+    result["varlen"] = {"kernel_tflops": tf, "kernel_ms": ms,
                         "unit": "TFLOP/s",
+                        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<bf16,128,...,DENSE=true>",
+                                     "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": tf / BF16_PEAK_TFLOPS,
+                                     "traffic": profiled_traffic("prefill_kernel_dense")},
                         "bits": "all rows equal to the paged prefill of the same keys and values",
                         "config": {"workload": "the prefill workload with dense keys and values "
                                                "[rows][Hkv][D] (bi_attn_varlen)"}}
@@ -517,8 +521,9 @@ def main():
                     help="measure the prefill workload alone (no headline value)")
     ap.add_argument("--cpu-samples", type=int, default=64)
     ap.add_argument("--profile-run", action="store_true",
-                    help="only the headline decode steps and the prefill workload (no split-by-batch "
-                         "variant, no batch sweep), so a profiler sees one workload per kernel")
+                    help="only the headline decode steps and the prefill workload, paged and dense (no "
+                         "split-by-batch variant, no batch sweep), so a profiler sees one workload "
+                         "per kernel")
     ap.add_argument("--next-rows-only", action="store_true",
                     help="only the RMSNorm and GEMM legs (no headline value; for profiling those kernels)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
