@@ -101,7 +101,13 @@ def load() -> ctypes.CDLL:
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a dense GPU tensor: the kernels index plain row-major memory, so a
+    strided view or a host tensor is refused here rather than read wrongly."""
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise BiAttnError(BI_EINVAL, "tensor arguments must be contiguous GPU tensors")
+    return t.data_ptr()
 
 
 def _stream(stream) -> Optional[int]:
@@ -203,6 +209,8 @@ def bi_rmsnorm(x: torch.Tensor, weight: torch.Tensor, y: torch.Tensor, eps: floa
     and dtype) with ``weight [hidden]``; one wavefront reduces each row."""
     if x.dtype not in (torch.bfloat16, torch.float32) or y.dtype != x.dtype or weight.dtype != x.dtype:
         raise BiAttnError(BI_EINVAL, "bi_rmsnorm")
+    if x.dim() != 2 or tuple(y.shape) != tuple(x.shape) or tuple(weight.shape) != (x.shape[1],):
+        raise BiAttnError(BI_EINVAL, "bi_rmsnorm")
     st = load().bi_rmsnorm(_ptr(x), _ptr(weight), _ptr(y), x.shape[0], x.shape[1],
                            BI_BF16 if x.dtype == torch.bfloat16 else BI_F32, float(eps),
                            _stream(stream))
@@ -214,7 +222,8 @@ def bi_gemm(a: torch.Tensor, w: torch.Tensor, c: torch.Tensor, stream=None) -> N
     bf16; N a multiple of 128, K a multiple of 64."""
     if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or c.dtype not in (torch.float32, torch.bfloat16):
         raise BiAttnError(BI_EINVAL, "bi_gemm")
-    if a.shape[1] != w.shape[1] or c.shape[0] != a.shape[0] or c.shape[1] != w.shape[0]:
+    if a.dim() != 2 or w.dim() != 2 or c.dim() != 2 or a.shape[1] != w.shape[1] or \
+            c.shape[0] != a.shape[0] or c.shape[1] != w.shape[0]:
         raise BiAttnError(BI_EINVAL, "bi_gemm")
     st = load().bi_gemm(_ptr(a), _ptr(w), _ptr(c), a.shape[0], w.shape[0], a.shape[1],
                         1 if c.dtype == torch.bfloat16 else 0, _stream(stream))

@@ -110,3 +110,23 @@ def test_workspace_bytes_formula():
         J = (L + 255) // 256
         ml = (rows * 64 * J * 8 + 255) // 256 * 256
         assert lib.bi_attn_workspace_bytes(ctypes.byref(c), rows, L) == ml + rows * 64 * J * 128 * 4
+
+
+def test_bindings_refuse_host_and_strided_tensors():
+    """The binding hands the kernels raw row-major addresses, so it refuses host tensors and
+    strided views (with an error, before any GPU call) instead of letting them be misread."""
+    import torch
+
+    import invariant_attention_amd as bi
+
+    a = torch.zeros((4, 64), dtype=torch.bfloat16)
+    w = torch.zeros((128, 64), dtype=torch.bfloat16)
+    c = torch.zeros((4, 128), dtype=torch.float32)
+    with pytest.raises(bi.BiAttnError):
+        bi.bi_gemm(a, w, c)
+    x = torch.zeros((3, 512))[:, :256]
+    assert not x.is_contiguous()
+    with pytest.raises(bi.BiAttnError):
+        bi.bi_rmsnorm(x, torch.ones(256), torch.zeros((3, 256)), 1e-6)
+    with pytest.raises(bi.BiAttnError):    # weight of the wrong length: refused before any call
+        bi.bi_rmsnorm(torch.zeros((3, 256)), torch.ones(255), torch.zeros((3, 256)), 1e-6)
