@@ -532,7 +532,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this path is built and timed on a single device "
-              "(see the sharding paragraph of DESIGN.md); run with --gpus 1.", file=sys.stderr)
+              "(the library has no multi-GPU path); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
