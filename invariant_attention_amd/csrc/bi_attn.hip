@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
       else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
     };
     subtile_step<E, D, NB>(st, qf, posv, getK, getV, a.cscale, key0, g, u.w0 + t == 0,
-                                  key0 + kSubTile - 1 > pos, lov, lo);
+                                  key0 + kSubTile - 1 > pos, lov);
   };
   // Every sub-tile of unit u, its first one already in flight in b0. Even sub-tiles are
   // computed from b0 and odd ones from b1; the next unit's first sub-tile goes to b0, during
@@ -677,14 +677,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
     for (int mb = 0; mb < NM; ++mb) Areg[AREG ? cb : 0][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // P_lo choice of the rows (their positions are fixed for the whole tile)
-  bool lo_c[NBW], lo_any_c = false;
+  // position part of the P_lo choice (the positions are fixed for the whole tile)
+  bool lo_c[NBW];
 #pragma unroll
-  for (int cb = 0; cb < NBW; ++cb) {
-    lo_c[cb] = needs_lo(pos_c[cb]);
-    lo_any_c = lo_any_c || lo_c[cb];
-  }
-  const bool lo_w = wave_any(lo_any_c);
+  for (int cb = 0; cb < NBW; ++cb) lo_c[cb] = needs_lo(pos_c[cb]);
   const int nsub = bad_seq ? 0 : (pos_max_wg + kSubTile) / kSubTile;
   // page ids of the logical pages the tile reads, in an LDS ring of kPageCache entries
   // (logical page lp in slot lp % kPageCache), refilled half a ring ahead of use
@@ -800,7 +796,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
       // all blocks advance together; on the diagonal of the tile the mask leaves rows whose
       // position is below key0 as they are (see subtile_step)
       subtile_step<E, D, NBW, BF>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
-                                  key0 + kSubTile - 1 > wave_min, lo_c, lo_w);
+                                  key0 + kSubTile - 1 > wave_min, lo_c);
     }
     if (last_of_split && wave_max >= j * S) {
       // fold split j into the rows of every block that reaches it (also when this wave's rows

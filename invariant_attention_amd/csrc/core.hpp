@@ -353,16 +353,30 @@ template <int D> struct Frag<float, D> {
 // l is kept per lane (the sum of the p values the lane holds); the row's l is the sum of its
 // four lanes' partials, taken once per split by row_l().
 constexpr float kLazy = 8.0f;
-// Precision of P in the bf16 PV product: a row at position < kLoKeys (fewer than kLoKeys + 1
-// keys, where a single bf16 P would leave errors near the tolerance) also adds the P_lo term;
-// longer rows use P_hi = bf16(p) alone, as bf16 attention kernels do. A function of the row's
-// position only, so every route makes the same choice.
+// Precision of P in the bf16 PV product. P_hi = bf16(p) alone carries a relative error up to
+// 2^-9 per key, which reaches the output in proportion to the key's share of the softmax: a
+// few keys carrying most of the weight pass it on almost whole. The P_lo term (p - P_hi, a
+// second bf16) is added for the keys of a lane when any of these holds:
+//   * the row is at a position below kLoKeys (few keys, so every key's share is large);
+//   * the row's split is peaked: from the sub-tile on where some lane of the row holds a
+//     scaled score more than kGap (base-2 units) above the mean of the row's unmasked scaled
+//     scores in the split's first sub-tile, to the end of the split (N(0,1)-like rows put
+//     their largest scores about 3 above that mean and rarely pass 6, sharper softmaxes pass
+//     it within a sub-tile or two);
+//   * the lane holds a key more than 2^kOver above the reference (an outlier that the lazy
+//     reference did not absorb).
+// Each decision depends only on the row's own scores, position and state, so every route
+// takes the same one; lanes without P_lo add exact zeros.
 constexpr int kLoKeys = 1024;
+constexpr float kGap = 6.0f;
+constexpr float kOver = 4.0f;
 __device__ __forceinline__ bool needs_lo(int pos) { return pos >= 0 && pos < kLoKeys; }
 
 template <int D> struct RowState {
   static constexpr int NM = D / 16;
   float m, l;
+  float thr;   // mean of the scaled scores of the split's first sub-tile + kGap (NaN: none)
+  bool lo;     // the split has turned out peaked: P_lo for its keys from then on
   f32x4 acc[NM];
 };
 template <int D> __device__ __forceinline__ float row_l(const RowState<D>& st) { return xor_sum(st.l); }
@@ -375,8 +389,8 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 //   pos[b]        -> this lane's row position in block b
 //   first: first sub-tile of the split (state reset, not rescaled)
 //   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
-//   lo_row[b]: needs_lo(pos[b]); lo_any: some lane of the wave has lo_row (wave-uniform); both
-//          depend on the positions only, so callers compute them once
+//   lo_pos[b]: needs_lo(pos[b]) (depends on the position only, so callers compute it once);
+//          the split and outlier parts of the P_lo choice are taken here
 //   A row with pos < key0 (all its keys masked) takes p = 0 everywhere, which leaves its state
 //   bitwise as it was; at a split start it gets the empty state (m = -FLT_MAX, l = 0,
 //   acc = 0), which the ascending fold leaves bitwise unchanged (a = 1, b = 0).
@@ -386,7 +400,7 @@ template <typename E, int D, int NB, bool PIPE = false, class KGet, class VGet>
 __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Frag<E, D>::Q* q,
                                              const int* pos, KGet&& getK, VGet&& getV,
                                              float cscale, int key0, int g, bool first,
-                                             bool mask, const bool (&lo_row)[NB], bool lo_any) {
+                                             bool mask, const bool (&lo_pos)[NB]) {
   using F = Frag<E, D>;
   constexpr int NM = D / 16;
   typename F::Q qv[NB];
@@ -434,11 +448,28 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     unsigned long long need_any = 0;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float mt = xor_max(mxl[b]) * cscale;
+      const float rm = xor_max(mxl[b]);
+      const float mt = rm * cscale;
       if (first) {
         // an all-masked row (a prefill row below the split's first key) takes the reference
         // -FLT_MAX, so its p = 2^-inf = 0 with a finite offset
         mnew[b] = mt > -3.40282347e38f ? mt : -3.40282347e38f;
+        // threshold of the peaked-split test: mean of the row's unmasked scaled scores + kGap,
+        // the lane sums in a fixed order and the row sums by the xor butterfly (every lane of
+        // the row gets the same bits); an all-masked row gets NaN, which never tests true
+        float sum = 0.f, cnt = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool in = x[b][kb][r] > -__builtin_inff();
+            sum = sum + (in ? x[b][kb][r] : 0.f);
+            cnt = cnt + (in ? 1.f : 0.f);
+          }
+        sum = xor_sum(sum);
+        cnt = xor_sum(cnt);
+        st[b].thr = (sum * cscale) / cnt + kGap;
+        st[b].lo = false;
       } else {
         const bool need = mt > st[b].m + kLazy;
         if (need) {
@@ -473,6 +504,21 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
   }
+  // P_lo choice of this lane's keys (position, peaked split, outlier above the reference).
+  // The peaked flag is per row: a ballot of the lanes above the threshold, read out for the
+  // lanes c, c + 16, c + 32, c + 48 of this lane's row.
+  bool lo_row[NB];
+  bool lo_lane = false;
+  const int col = (int)(threadIdx.x & 15);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float xm = mxl[b] * cscale;
+    const unsigned long long up = __builtin_amdgcn_ballot_w64(xm > st[b].thr);
+    st[b].lo = st[b].lo || ((up >> col) & 0x0001000100010001ull) != 0;
+    lo_row[b] = lo_pos[b] || st[b].lo || xm > mnew[b] + kOver;
+    lo_lane = lo_lane || lo_row[b];
+  }
+  const bool lo_any = wave_any(lo_lane);
   f32x4 accl[NB][NM];
 #pragma unroll
   for (int b = 0; b < NB; ++b)

@@ -129,9 +129,9 @@ def test_run_to_run_determinism():
 
 
 # ----------------------------------------------------------------------------- routes
-def _chunked_route(shape, cfg, specs, chunk, seed):
+def _chunked_route(shape, cfg, specs, chunk, seed, q_scale=1.0):
     """Process every sequence's new tokens in chunks of ``chunk`` (1 => decode calls)."""
-    full = build_batch(shape, specs, seed=seed, page_seed=11)
+    full = build_batch(shape, specs, seed=seed, page_seed=11, q_scale=q_scale)
     d = to_device(full, cfg)
     # fresh NaN pool holding only the prefixes; tokens arrive chunk by chunk
     outs = torch.full((full.total_tokens, cfg.num_q_heads, cfg.head_dim), float("nan"), device="cuda")
@@ -210,6 +210,21 @@ def test_long_decode_batch_invariance():
             assert_bitwise(out, ref[start:start + B], f"long B={B} start={start}")
 
 
+def test_peaked_route_invariance():
+    """q x 4 rows at positions 1024 .. 4095, where the second bf16 term of P follows the scores
+    (peaked splits, outliers above the lazy reference) rather than the position alone: one
+    prefill, chunks of 512 and 128, and token-by-token decode give identical bits."""
+    shape = AttnShape(64, 4, 128, 16, 256, "bf16")
+    cfg = cfg_for(shape)
+    specs = [SeqSpec(0, 1024, 3072), SeqSpec(1, 2000, 300), SeqSpec(2, 0, 700)]
+    _print_case("peaked routes")
+    ref, full = _chunked_route(shape, cfg, specs, 1 << 30, seed=63, q_scale=4.0)
+    for ch in (512, 128, 1):
+        got, _ = _chunked_route(shape, cfg, specs, ch, seed=63, q_scale=4.0)
+        assert_bitwise(got, ref, f"peaked: chunk {ch} vs one prefill")
+        _print_case("peaked route ok", ch)
+
+
 # ----------------------------------------------------------------------------- negative control
 def test_split_by_batch_variant_changes_bits():
     """The batch-dependent split policy must show more than one bit pattern for a probe."""
@@ -255,16 +270,18 @@ def test_p_precision_boundary_route_invariance(hq):
         assert_bitwise(got, ref, f"chunk {ch} vs one prefill across the P precision boundary")
 
 
-@pytest.mark.parametrize("hq", [64, 32])
-def test_prefill_past_page_id_ring(hq):
-    """Sequences longer than the prefill kernel's LDS ring of 2048 page ids (32768 tokens), so
-    the ring is refilled while the tile runs: a 40000-token prefix with a 70-token chunk and
-    a shorter neighbour. One prefill, chunks of 16 and decode give identical bits; sampled rows
-    match the oracle."""
-    shape = AttnShape(hq, 4, 128, 16, 256, "bf16")
+@pytest.mark.parametrize("hq,dtype,d", [(64, "bf16", 128), (32, "bf16", 128), (32, "f32", 128),
+                                        (16, "bf16", 64), (8, "f32", 64)])
+def test_prefill_past_page_id_ring(hq, dtype, d):
+    """Sequences past 32768 tokens: a 40000-token prefix with a 70-token chunk and a shorter
+    neighbour. bf16 with D = 128 streams K/V straight into LDS with page ids in registers; fp32,
+    and bf16 with D = 64, stage K/V through registers and read page ids from an LDS ring of 2048
+    entries, which is refilled while the tile runs past 32768 tokens. One prefill, chunks of 16
+    and decode give identical bits; sampled rows match the oracle."""
+    shape = AttnShape(hq, 4, d, 16, 256, dtype)
     cfg = cfg_for(shape)
     specs = [SeqSpec(0, 40000, 70), SeqSpec(1, 33000, 5)]
-    _print_case("ring", hq)
+    _print_case("ring", hq, dtype, d)
     ref, full = _chunked_route(shape, cfg, specs, 1 << 30, seed=91)
     for ch in (16, 1):
         got, _ = _chunked_route(shape, cfg, specs, ch, seed=91)
