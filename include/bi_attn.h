@@ -148,7 +148,14 @@ int bi_attn_decode_combine(const bi_attn_cfg* cfg, const int32_t* seq_lens, int3
  * reads all keys, prefix and chunk, through the page table (liuwei.blog post, section
  * 破解之道：重塑GPU内核: a token's reduction must not depend on whether its keys arrive as
  * a prefill block or from a full cache). max_q_len >= every n_new[b]; max_seq_len >= every
- * seq_lens[b]. workspace may be NULL (not used).
+ * seq_lens[b]; q_starts non-decreasing from q_starts[0] >= 0 to q_starts[batch] <=
+ * total_tokens. A sequence that breaks these (n_new[b] > max_q_len, q_starts[b+1] >
+ * total_tokens, n_new[b] > seq_lens[b], seq_lens[b] > max_seq_len) gets NaN in its rows that
+ * lie in q (rows q_starts[b] .. min(q_starts[b+1], total_tokens) - 1); a pair of q_starts
+ * entries out of order gives the sequence no rows; the rows of every other sequence are
+ * computed as usual (with q_starts out of order, rows claimed by two sequences are
+ * unspecified). Nothing outside q, out and the caches is read or written.
+ * workspace may be NULL (not used).
  */
 int bi_attn_prefill(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* page_table, int32_t max_pages,
@@ -167,8 +174,9 @@ int bi_attn_prefill(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
  * item): this call runs the prefill kernel's arithmetic on the dense layout, so each output
  * row is bit-identical to bi_attn_prefill / bi_attn_decode on the same keys and values held
  * in a paged cache (any page placement, any batch, any chunking), within one build on one
- * device. A sequence whose k_starts entries are out of range, or with n_new > seq_len or
- * seq_len > max_seq_len, gets NaN rows. max_q_len >= every n_new[b]. No workspace.
+ * device. A sequence whose k_starts entries are out of range, or with n_new > seq_len,
+ * seq_len > max_seq_len, n_new > max_q_len or q_starts[b+1] > total_q, gets NaN rows (those
+ * that lie in q), as in bi_attn_prefill. max_q_len >= every n_new[b]. No workspace.
  */
 int bi_attn_varlen(const bi_attn_cfg* cfg, const void* q, const void* k, const void* v,
                    const int32_t* q_starts, const int32_t* k_starts, int32_t batch,

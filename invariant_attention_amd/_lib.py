@@ -110,6 +110,29 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(t: Optional[torch.Tensor], where: str, name: str, dtype: torch.dtype,
+            shape: tuple) -> None:
+    """Refuse a tensor of the wrong dtype or shape (``None`` in ``shape`` matches any size)
+    before anything reaches the library: the kernels index raw memory by the sizes they are
+    given, so a mismatch would be read or written past the tensor instead of failing."""
+    if t is None:
+        raise BiAttnError(BI_EINVAL, f"{where}: {name} is missing")
+    if t.dtype != dtype:
+        raise BiAttnError(BI_EINVAL, f"{where}: {name} must be {dtype}, got {t.dtype}")
+    if t.dim() != len(shape) or any(want is not None and int(got) != want
+                                    for got, want in zip(t.shape, shape)):
+        raise BiAttnError(BI_EINVAL, f"{where}: {name} must have shape {shape}, got {tuple(t.shape)}")
+
+
+def _check_cache(cfg: "AttnConfig", where: str, k_cache: torch.Tensor, v_cache: torch.Tensor) -> int:
+    """Both caches ``[num_pages][Hkv][page_size][D]`` of the configured dtype; returns
+    num_pages."""
+    dt = cfg.torch_dtype
+    _expect(k_cache, where, "k_cache", dt, (None, cfg.num_kv_heads, cfg.page_size, cfg.head_dim))
+    _expect(v_cache, where, "v_cache", dt, tuple(k_cache.shape))
+    return int(k_cache.shape[0])
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -133,6 +156,14 @@ def bi_kv_page_update(cfg: AttnConfig, k_new: torch.Tensor, v_new: torch.Tensor,
                       q_starts: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
                       k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
     """Write a step's new K/V rows into their pages (before attention, same stream)."""
+    w = "bi_kv_page_update"
+    _check_cache(cfg, w, k_cache, v_cache)
+    _expect(k_new, w, "k_new", cfg.torch_dtype, (None, cfg.num_kv_heads, cfg.head_dim))
+    _expect(v_new, w, "v_new", cfg.torch_dtype, tuple(k_new.shape))
+    _expect(seq_lens, w, "seq_lens", torch.int32, (None,))
+    B = int(seq_lens.shape[0])
+    _expect(q_starts, w, "q_starts", torch.int32, (B + 1,))
+    _expect(page_table, w, "page_table", torch.int32, (B, None))
     st = load().bi_kv_page_update(
         ctypes.byref(cfg.c()), _ptr(k_new), _ptr(v_new), _ptr(q_starts), _ptr(seq_lens),
         _ptr(page_table), page_table.shape[1], k_cache.shape[0], seq_lens.shape[0],
@@ -144,12 +175,24 @@ def bi_attn_decode(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_ca
                    page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                    out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     """One query token per sequence; ``out`` fp32 ``[batch][Hq][D]``."""
+    _check_decode(cfg, "bi_attn_decode", q, k_cache, v_cache, page_table, seq_lens, out)
     st = load().bi_attn_decode(
         ctypes.byref(cfg.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         page_table.shape[1], k_cache.shape[0], _ptr(seq_lens), seq_lens.shape[0],
         int(max_seq_len), _ptr(out), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "bi_attn_decode")
+
+
+def _check_decode(cfg: AttnConfig, w: str, q, k_cache, v_cache, page_table, seq_lens, out) -> None:
+    _expect(seq_lens, w, "seq_lens", torch.int32, (None,))
+    B = int(seq_lens.shape[0])
+    if q is not None or k_cache is not None:
+        _check_cache(cfg, w, k_cache, v_cache)
+        _expect(q, w, "q", cfg.torch_dtype, (B, cfg.num_q_heads, cfg.head_dim))
+        _expect(page_table, w, "page_table", torch.int32, (B, None))
+    if out is not None:
+        _expect(out, w, "out", torch.float32, (B, cfg.num_q_heads, cfg.head_dim))
 
 
 def _nbytes(t: Optional[torch.Tensor]) -> int:
@@ -161,6 +204,7 @@ def bi_attn_decode_partials(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Ten
                             seq_lens: torch.Tensor, max_seq_len: int, workspace: torch.Tensor,
                             stream=None) -> None:
     """First phase of decode: split partials into ``workspace``."""
+    _check_decode(cfg, "bi_attn_decode_partials", q, k_cache, v_cache, page_table, seq_lens, None)
     st = load().bi_attn_decode_partials(
         ctypes.byref(cfg.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         page_table.shape[1], k_cache.shape[0], _ptr(seq_lens), seq_lens.shape[0],
@@ -171,6 +215,7 @@ def bi_attn_decode_partials(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Ten
 def bi_attn_decode_combine(cfg: AttnConfig, seq_lens: torch.Tensor, max_seq_len: int,
                            out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     """Second phase of decode: ascending fold of the partials into ``out``."""
+    _check_decode(cfg, "bi_attn_decode_combine", None, None, None, None, seq_lens, out)
     st = load().bi_attn_decode_combine(
         ctypes.byref(cfg.c()), _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(out),
         _ptr(workspace), _nbytes(workspace), _stream(stream))
@@ -182,6 +227,14 @@ def bi_attn_prefill(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_c
                     max_q_len: int, max_seq_len: int, out: torch.Tensor,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Chunked prefill of ``q [T][Hq][D]``; ``out`` fp32 ``[T][Hq][D]``."""
+    w = "bi_attn_prefill"
+    _check_cache(cfg, w, k_cache, v_cache)
+    _expect(q, w, "q", cfg.torch_dtype, (None, cfg.num_q_heads, cfg.head_dim))
+    _expect(out, w, "out", torch.float32, tuple(q.shape))
+    _expect(seq_lens, w, "seq_lens", torch.int32, (None,))
+    B = int(seq_lens.shape[0])
+    _expect(q_starts, w, "q_starts", torch.int32, (B + 1,))
+    _expect(page_table, w, "page_table", torch.int32, (B, None))
     st = load().bi_attn_prefill(
         ctypes.byref(cfg.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         page_table.shape[1], k_cache.shape[0], _ptr(q_starts), _ptr(seq_lens),
@@ -196,6 +249,13 @@ def bi_attn_varlen(cfg: AttnConfig, q: torch.Tensor, k: torch.Tensor, v: torch.T
                    max_seq_len: int, out: torch.Tensor, stream=None) -> None:
     """Dense varlen attention: ``k``, ``v`` ``[total_k][Hkv][D]``, sequence ``b`` owning rows
     ``k_starts[b] .. k_starts[b+1]-1``; ``q [T][Hq][D]``; ``out`` fp32 ``[T][Hq][D]``."""
+    w = "bi_attn_varlen"
+    _expect(q, w, "q", cfg.torch_dtype, (None, cfg.num_q_heads, cfg.head_dim))
+    _expect(out, w, "out", torch.float32, tuple(q.shape))
+    _expect(k, w, "k", cfg.torch_dtype, (None, cfg.num_kv_heads, cfg.head_dim))
+    _expect(v, w, "v", cfg.torch_dtype, tuple(k.shape))
+    _expect(k_starts, w, "k_starts", torch.int32, (None,))
+    _expect(q_starts, w, "q_starts", torch.int32, tuple(k_starts.shape))
     st = load().bi_attn_varlen(
         ctypes.byref(cfg.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(q_starts), _ptr(k_starts),
         k_starts.shape[0] - 1, q.shape[0], k.shape[0], int(max_q_len), int(max_seq_len),

@@ -517,14 +517,21 @@ constexpr int kPageCache = 2048;
 // ascending, then t ascending), so the longest tiles start first and the short ones fill the
 // end of the grid. Which workgroup computes an item never changes its numbers.
 struct PfSeq {
-  int fp, n, nt;   // first position, new tokens, tiles (0: the sequence has no items)
-  bool bad;        // invalid lengths: its tiles cost nothing (they only write NaN rows)
+  int q0;          // first row of q and out
+  int len;         // keys of the sequence (seq_lens[b], or the dense row range)
+  int fp, n, nt;   // first position, rows of q and out (n_new, clipped to total_tokens), tiles
+  bool bad;        // invalid sequence: its tiles cost nothing and only write NaN rows
 };
+// A sequence is invalid when its q_starts pair is out of order, starts outside q or ends past
+// total_tokens, has more new tokens than max_q_len or than its length, or its length or (dense)
+// key rows are out of range. Its rows that lie in q (rows q0 .. min(q1, total_tokens) - 1, none
+// when the pair is out of order or starts outside q) come out NaN; other sequences' rows are
+// untouched.
 __device__ __forceinline__ PfSeq pf_seq(const AttnParams& a, int b, int tq) {
-  PfSeq s{0, 0, 0, false};
+  PfSeq s{0, 0, 0, 0, 0, false};
   if (b >= a.batch) return s;
   const int q0 = a.q_starts[b], q1 = a.q_starts[b + 1];
-  if (q1 > a.total_tokens || q0 < 0 || q1 <= q0) return s;
+  if (q0 < 0 || q1 < q0 || q0 >= a.total_tokens) return s;
   int len;
   bool rows_ok = true;
   if (a.k_starts) {
@@ -534,10 +541,15 @@ __device__ __forceinline__ PfSeq pf_seq(const AttnParams& a, int b, int tq) {
   } else {
     len = a.seq_lens[b];
   }
-  s.n = q1 - q0;
-  s.nt = (s.n + tq - 1) / tq;
-  s.bad = len > a.max_seq_len || s.n > len || !rows_ok;
-  s.fp = len - s.n;
+  const int n_new = q1 - q0;
+  s.q0 = q0;
+  s.len = len;
+  s.n = min(q1, a.total_tokens) - q0;
+  // tiles, at most max_q_len / tq per sequence, so the grid always holds every item (an
+  // invalid sequence with more rows covers them in strides; a valid one is never capped)
+  s.nt = min((s.n + tq - 1) / tq, (a.max_q_len + tq - 1) / tq);
+  s.bad = q1 > a.total_tokens || n_new > a.max_q_len || len > a.max_seq_len || n_new > len || !rows_ok;
+  s.fp = len - n_new;
   return s;
 }
 // tiles of the sequence whose sub-tile count exceeds K (K >= -1): n(b, t) > K exactly when
@@ -625,14 +637,30 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   const int kvh = (int)(blockIdx.x % (unsigned)a.hkv);
   int b = 0, tile = 0;
   if (!pf_item(a, tq, (int)(blockIdx.x / (unsigned)a.hkv), b, tile)) return;
-  const int q0 = a.q_starts[b], q1 = a.q_starts[b + 1];
-  const int n_new = q1 - q0;
+  const PfSeq sq = pf_seq(a, b, tq);
+  const int q0 = sq.q0;
+  const int n_new = sq.n;                 // rows of this sequence in q and out
   const int t0 = tile * tq;
   // dense: the sequence's keys are rows k0 .. k0 + seq_len - 1 of [k_rows][Hkv][D] arrays
   const int k0 = DENSE ? a.k_starts[b] : 0;
-  const int seq_len = DENSE ? a.k_starts[b + 1] - k0 : a.seq_lens[b];
-  const bool bad_seq = seq_len > a.max_seq_len || n_new > seq_len || (DENSE && (k0 < 0 || k0 + seq_len > a.k_rows));
-  const int first_pos = seq_len - n_new;
+  const int seq_len = sq.len;
+  const bool bad_seq = sq.bad;
+  const int first_pos = sq.fp;
+  if (bad_seq) {
+    // an invalid sequence: NaN rows only; its tiles (at most max_q_len / tq of them) cover
+    // rows t0 + k * (tiles * tq), k = 0, 1, ..., of every column
+    const int rstep = sq.nt * tq;
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) {
+      const int col = (wave * NBW + cb) * 16 + c;
+      for (int tok = t0 + col / G; tok < n_new; tok += rstep) {
+        float* dst = a.out + ((size_t)(q0 + tok) * a.hq + kvh * G + col % G) * D + g * (D / 4);
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) *(f32x4*)(dst + 4 * i) = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      }
+    }
+    return;
+  }
   const int t_last = min(t0 + tq, n_new) - 1;
   const int pos_max_wg = first_pos + t_last;
   const int S = split_len(a, seq_len);
@@ -1230,7 +1258,8 @@ int launch_prefill(const AttnParams& a, hipStream_t s) {
   // sequences longer than the LDS page-id ring need the kernel that refills it (paged layout)
   const bool ring = !DENSE && (int64_t)a.max_seq_len + kSubTile > (int64_t)kPageCache * kPage;
   const int tq = NW * NBW * 16 / a.group;
-  // one workgroup per (tile, KV head); workgroups past the real item count exit at once
+  // one workgroup per (tile, KV head): every sequence has at most ceil(max_q_len / tq) tiles,
+  // so the grid holds every item; workgroups past the real item count exit at once
   const int64_t wgs = (int64_t)((a.max_q_len + tq - 1) / tq) * a.batch * a.hkv;
   if (wgs > 0x7fffffff) return BI_EUNSUPPORTED;
   const dim3 grid((unsigned)wgs);

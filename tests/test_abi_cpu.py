@@ -130,3 +130,59 @@ def test_bindings_refuse_host_and_strided_tensors():
         bi.bi_rmsnorm(x, torch.ones(256), torch.zeros((3, 256)), 1e-6)
     with pytest.raises(bi.BiAttnError):    # weight of the wrong length: refused before any call
         bi.bi_rmsnorm(torch.zeros((3, 256)), torch.ones(255), torch.zeros((3, 256)), 1e-6)
+
+
+def test_bindings_refuse_wrong_dtypes_and_shapes():
+    """Every attention entry point checks each tensor's dtype against cfg.dtype (index arrays
+    int32, out fp32) and its shape against the configured heads, head_dim and page size, before
+    any GPU call: a mismatch would otherwise be read or written past the tensor."""
+    import torch
+
+    cfg = bi.AttnConfig(**BASE)           # bf16, Hq 64, Hkv 4, D 128, page 16
+    B, T, P = 2, 5, 6
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+
+    def good():
+        return dict(q=torch.zeros((T, 64, 128), dtype=bf), kc=torch.zeros((P, 4, 16, 128), dtype=bf),
+                    vc=torch.zeros((P, 4, 16, 128), dtype=bf), pt=torch.zeros((B, 3), dtype=i32),
+                    qs=torch.zeros(B + 1, dtype=i32), sl=torch.zeros(B, dtype=i32),
+                    out=torch.zeros((T, 64, 128), dtype=f32), kn=torch.zeros((T, 4, 128), dtype=bf))
+
+    def prefill(**kw):
+        a = {**good(), **kw}
+        bi.bi_attn_prefill(cfg, a["q"], a["kc"], a["vc"], a["pt"], a["qs"], a["sl"], 4, 64, a["out"])
+
+    def decode(**kw):
+        a = {**good(), **kw}
+        q = a["q"][:B] if "q" not in kw else a["q"]
+        out = a["out"][:B] if "out" not in kw else a["out"]
+        bi.bi_attn_decode(cfg, q, a["kc"], a["vc"], a["pt"], a["sl"], 64, out, torch.zeros(8))
+
+    def update(**kw):
+        a = {**good(), **kw}
+        bi.bi_kv_page_update(cfg, a["kn"], a["kn"] if "kn" in kw else a["kn"].clone(), a["qs"],
+                             a["sl"], a["pt"], a["kc"], a["vc"])
+
+    bad_cases = [
+        (prefill, dict(q=torch.zeros((T, 64, 128), dtype=f32)), "q must be"),           # fp32 q, bf16 cfg
+        (prefill, dict(out=torch.zeros((T, 64, 128), dtype=bf)), "out must be"),         # bf16 out
+        (prefill, dict(kc=torch.zeros((P, 4, 16, 128), dtype=f32)), "k_cache must be"),
+        (prefill, dict(kc=torch.zeros((P * 64, 128), dtype=bf)), "k_cache must have"),   # flattened
+        (prefill, dict(vc=torch.zeros((P, 4, 16, 64), dtype=bf)), "v_cache must have"),
+        (prefill, dict(q=torch.zeros((T, 32, 128), dtype=bf)), "q must have"),           # wrong Hq
+        (prefill, dict(qs=torch.zeros(B, dtype=i32)), "q_starts must have"),             # B, not B+1
+        (prefill, dict(qs=torch.zeros(B + 1, dtype=torch.int64)), "q_starts must be"),
+        (prefill, dict(pt=torch.zeros((B + 1, 3), dtype=i32)), "page_table must have"),
+        (prefill, dict(out=torch.zeros((T + 1, 64, 128), dtype=f32)), "out must have"),
+        (decode, dict(q=torch.zeros((B + 1, 64, 128), dtype=bf)), "q must have"),        # q rows != batch
+        (decode, dict(out=torch.zeros((B, 64, 128), dtype=bf)), "out must be"),
+        (decode, dict(sl=torch.zeros(B, dtype=torch.int64)), "seq_lens must be"),
+        (update, dict(kn=torch.zeros((T, 4, 128), dtype=f32)), "k_new must be"),
+        (update, dict(pt=torch.zeros((B, 3), dtype=torch.int16)), "page_table must be"),
+    ]
+    for fn, kw, msg in bad_cases:
+        with pytest.raises(bi.BiAttnError, match=msg):
+            fn(**kw)
+    # well-formed host tensors pass the checks and are then refused as host tensors
+    with pytest.raises(bi.BiAttnError, match="contiguous GPU tensors"):
+        prefill()

@@ -225,6 +225,57 @@ def test_peaked_route_invariance():
         _print_case("peaked route ok", ch)
 
 
+def test_decode_two_phases_equal_one_call():
+    """bi_attn_decode_partials then bi_attn_decode_combine on the same workspace give the bits
+    of bi_attn_decode (the route the benchmark times), also from a NaN-poisoned workspace and
+    for sequences of 1 to 64 splits."""
+    shape = CONFIG_SHAPES["decode_bf16"]
+    cfg = cfg_for(shape)
+    rng = np.random.default_rng(81)
+    lens = [1, 255, 256, 257, 16384, 16385] + [int(x) for x in rng.integers(128, 8193, 26)]
+    bt = build_batch(shape, [SeqSpec(i, L - 1, 1) for i, L in enumerate(lens)], seed=82, page_seed=83)
+    d = to_device(bt, cfg)
+    page_update(cfg, d)
+    B, mx = len(lens), bt.max_seq_len
+    ref = _decode_sub(cfg, d, list(range(B)), mx)
+    ws = decode_workspace(cfg, B, mx)                   # NaN-filled
+    out = torch.full_like(ref, float("nan"))
+    bi.bi_attn_decode_partials(cfg, d.q, d.k_cache, d.v_cache, d.page_table, d.seq_lens, mx, ws)
+    bi.bi_attn_decode_combine(cfg, d.seq_lens, mx, out, ws)
+    assert_bitwise(out, ref, "partials + combine vs one decode call")
+
+
+def test_probe_unique_bit_patterns_over_1000_compositions():
+    """The kernel-level analogue of the pages' experiment (one prompt, 1000 runs, count the
+    distinct completions): a decode probe in 1000 random batch compositions (batch size 1..64,
+    random position, random neighbours from 200 sequences of the decode workload's lengths)
+    gives exactly one bit pattern; the split-by-batch variant gives more than one."""
+    shape = CONFIG_SHAPES["decode_bf16"]
+    cfg = cfg_for(shape)
+    cfg_v = cfg_for(shape, policy=bi.BI_SPLIT_BY_BATCH)
+    rng = np.random.default_rng(2026)
+    lens = [4097] + [int(x) for x in rng.integers(128, 8193, 200)]
+    bt = build_batch(shape, [SeqSpec(i, L - 1, 1) for i, L in enumerate(lens)], seed=2026, page_seed=84)
+    d = to_device(bt, cfg)
+    page_update(cfg, d)
+    mx = 8192
+    ws = torch.empty(bi.bi_attn_workspace_bytes(cfg_v, 64, mx) // 4 + 64, device="cuda")
+    patterns, patterns_v = set(), set()
+    for trial in range(1000):
+        B = int(rng.integers(1, 65))
+        p = int(rng.integers(0, B))
+        nb = [int(x) + 1 for x in rng.choice(200, B - 1, replace=False)]
+        idx = nb[:p] + [0] + nb[p:]
+        patterns.add(bits(_decode_sub(cfg, d, idx, mx, ws)[p]).tobytes())
+        patterns_v.add(bits(_decode_sub(cfg_v, d, idx, mx, ws)[p]).tobytes())
+        if trial % 250 == 0:
+            _print_case("composition", trial, len(patterns), len(patterns_v))
+    print(f"1000 compositions: {len(patterns)} bit pattern(s) with the fixed split size, "
+          f"{len(patterns_v)} with the split count chosen by batch")
+    assert len(patterns) == 1
+    assert len(patterns_v) > 1
+
+
 # ----------------------------------------------------------------------------- negative control
 def test_split_by_batch_variant_changes_bits():
     """The batch-dependent split policy must show more than one bit pattern for a probe."""

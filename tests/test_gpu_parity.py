@@ -98,7 +98,8 @@ def test_split_edges_single_sequence():
     """Lengths at split and sub-tile edges, decode and prefill, against the oracle."""
     shape = AttnShape(32, 4, 128, 16, 256, "bf16")
     cfg = cfg_for(shape)
-    for L in (1, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 4095, 4096, 4097):
+    for L in (1, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 4095, 4096, 4097, 16383,
+              16384, 16385):
         bt = build_batch(shape, [SeqSpec(L, L - 1, 1)], seed=14)
         _print_case("edge", L)
         out = run_decode(cfg, to_device(bt, cfg)).cpu().numpy()
@@ -230,3 +231,38 @@ def test_prefill_many_sequences_with_invalid_lengths(hq):
     ref = oracle_rows(bt, rows)
     got = np.stack([clean[r, h].cpu().numpy() for r, h in rows])
     assert_parity(got, ref, "prefill 90 sequences, sampled rows")
+
+
+def test_prefill_invalid_chunks_give_nan_rows_only():
+    """A sequence with more new tokens than max_q_len, or whose q_starts entry runs past
+    total_tokens, is invalid: its rows that lie in q come out NaN (none is left unwritten), and
+    every other sequence's rows keep the bits of a clean run."""
+    shape = AttnShape(64, 4, 128, 16, 256, "bf16")
+    cfg = cfg_for(shape)
+    seqs = [SeqSpec(0, 300, 40), SeqSpec(1, 100, 200), SeqSpec(2, 50, 30), SeqSpec(3, 700, 60)]
+    bt = build_batch(shape, seqs, seed=71, page_seed=72, extra_pages=4)
+    d = to_device(bt, cfg)
+    clean = run_prefill(cfg, d)
+    assert torch.isfinite(clean).all()
+    T, qs = bt.total_tokens, bt.q_starts
+    _print_case("prefill n_new > max_q_len")
+    # sequence 1 has 200 new tokens; max_q_len 60 makes it invalid (its 200 rows need
+    # several strides of its capped tiles)
+    out = torch.zeros_like(clean)
+    bi.bi_attn_prefill(cfg, d.q, d.k_cache, d.v_cache, d.page_table, d.q_starts, d.seq_lens, 60,
+                       d.max_seq_len, out)
+    r0, r1 = int(qs[1]), int(qs[2])
+    assert torch.isnan(out[r0:r1]).all()
+    keep = torch.cat([torch.arange(0, r0), torch.arange(r1, T)]).cuda()
+    assert_bitwise(out[keep], clean[keep], "rows of valid sequences next to n_new > max_q_len")
+    _print_case("prefill q_starts past total_tokens")
+    # the last entry of q_starts 25 past the rows of q: the last sequence is invalid, its rows
+    # inside q are NaN, nothing is read or written past q and out
+    qs2 = d.q_starts.clone()
+    qs2[-1] = T + 25
+    out = torch.zeros_like(clean)
+    bi.bi_attn_prefill(cfg, d.q, d.k_cache, d.v_cache, d.page_table, qs2, d.seq_lens, d.max_q_len,
+                       d.max_seq_len, out)
+    r3 = int(qs[3])
+    assert torch.isnan(out[r3:]).all()
+    assert_bitwise(out[:r3], clean[:r3], "rows of valid sequences next to a q_starts overrun")
