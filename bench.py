@@ -7,10 +7,14 @@ largest batch (64 sequences, 32 query heads, 4 KV heads, head_dim 128, context l
 U[128, 8192], 16-token pages in a shuffled pool, fixed split size 256); ``value`` is its
 algorithmic HBM GB/s. The chunked-prefill workload (16 sequences, 64/4 heads, cached prefix
 U[0, 16384], new chunk U[1, 2048]) is measured in the same run and reported under
-``prefill`` in TFLOP/s. Every figure counts only because the same run checks parity against
-the fp64 oracle and bitwise batch invariance first.
+``prefill`` in TFLOP/s, the long-context decode (8 x 131072 tokens, q x 4) under
+``long_decode`` and the 64-step mixed continuous-batching trace under ``mixed_trace``.
+Times are reported as medians with p10/p90 beside the whole-run averages. Every figure counts
+only because the same run checks bitwise batch invariance first and, in the host leg, parity
+against the fp64 oracle (the headline decode rows, sampled prefill and long-context rows).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+                       [--no-long] [--no-trace]
 """
 
 from __future__ import annotations
@@ -77,6 +81,27 @@ def dev(x, dt):
 def cfg_of(shape, policy=bi.BI_SPLIT_FIXED):
     return bi.AttnConfig(shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.page_size,
                          shape.split_size, bi.BI_BF16, 0.0, policy)
+
+
+def stats_ms(samples):
+    """median / p10 / p90 / mean of per-iteration times, in microseconds."""
+    a = np.asarray(samples, np.float64) * 1e3
+    return {"median_us": float(np.median(a)), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90)), "mean_us": float(a.mean()), "n": int(a.size)}
+
+
+def host_cpu():
+    """CPU model and thread counts of the host (for the oracle's timing)."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
 
 
 class Timer:
@@ -149,9 +174,12 @@ def run_decode_bench(args, result):
                                       "reversed batch order; all rows equal"}
     gpu_out = ref_bits.cpu().double().numpy()
 
-    # --- the non-invariant comparison variant (split count chosen by batch)
+    # --- the non-invariant comparison variants (split count chosen by batch: about 2 splits
+    # per CU, and enough to fill the 8 resident waves per CU)
     cfg_v = cfg_of(shape, bi.BI_SPLIT_BY_BATCH)
-    ws_v = torch.empty(bi.bi_attn_workspace_bytes(cfg_v, B, mx) // 4 + 64, device="cuda")
+    cfg_f = cfg_of(shape, bi.BI_SPLIT_BY_BATCH_FILL)
+    ws_v = torch.empty(max(bi.bi_attn_workspace_bytes(c, B, mx) for c in (cfg_v, cfg_f)) // 4 + 64,
+                       device="cuda")
 
     def step(i, c, w, tm=None):
         kc, vc = pools[i % R]
@@ -163,28 +191,31 @@ def run_decode_bench(args, result):
         bi.bi_attn_decode_combine(c, sl, mx, out, w)
         if tm: tm.mark(3)
 
-    for i in range(args.warmup):
-        step(i, cfg, ws)
+    def whole_run(c, w):
+        for i in range(args.warmup):
+            step(i, c, w)
+        tm = Timer(2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tm.mark(0)
+        for i in range(args.steps):
+            step(i, c, w)
+        tm.mark(1)
+        torch.cuda.synchronize()
+        return tm.ms(0, 1) / args.steps, (time.perf_counter() - t0) / args.steps
+
     # the timed steps: nothing but the three calls per step (events only around the whole run)
-    whole = Timer(2)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    whole.mark(0)
-    for i in range(args.steps):
-        step(i, cfg, ws)
-    whole.mark(1)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
-    gpu_step = whole.ms(0, 1) / args.steps
+    gpu_step, wall = whole_run(cfg, ws)
     # per-kernel breakdown in a separate pass with events between the calls
     timers = [Timer(4) for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, cfg, ws, timers[i])
     torch.cuda.synchronize()
-    pu = np.mean([t.ms(0, 1) for t in timers])
-    comb = np.mean([t.ms(2, 3) for t in timers])
+    pu = [t.ms(0, 1) for t in timers]
+    comb = [t.ms(2, 3) for t in timers]
+    steps_ms = [t.ms(0, 3) for t in timers]
     # the dominant kernel alone: back-to-back launches on the same stream (rotating the pools),
-    # events around the whole run, so the average excludes the event records between calls
+    # events around each launch and around the whole run (the average excludes the records)
     tk = Timer(2)
     torch.cuda.synchronize()
     tk.mark(0)
@@ -194,20 +225,22 @@ def run_decode_bench(args, result):
     tk.mark(1)
     torch.cuda.synchronize()
     part = tk.ms(0, 1) / args.steps
+    part_each = []
+    for i in range(args.steps):
+        kc, vc = pools[i % R]
+        t1 = Timer(2)
+        t1.mark(0)
+        bi.bi_attn_decode_partials(cfg, q, kc, vc, pt, sl, mx, ws)
+        t1.mark(1)
+        part_each.append(t1)
+    torch.cuda.synchronize()
+    part_each = [t.ms(0, 1) for t in part_each]
 
     # variant timing (same step shape)
-    var_step = None
+    var_step = fill_step = None
     if not args.profile_run:
-        for i in range(args.warmup):
-            step(i, cfg_v, ws_v)
-        whole_v = Timer(2)
-        torch.cuda.synchronize()
-        whole_v.mark(0)
-        for i in range(args.steps):
-            step(i, cfg_v, ws_v)
-        whole_v.mark(1)
-        torch.cuda.synchronize()
-        var_step = whole_v.ms(0, 1) / args.steps
+        var_step = whole_run(cfg_v, ws_v)[0]
+        fill_step = whole_run(cfg_f, ws_v)[0]
 
     nb = decode_bytes(shape, bt.seq_lens)
     step_ms = max(wall * 1e3, gpu_step)
@@ -224,10 +257,19 @@ def run_decode_bench(args, result):
                           "frac": split_gbs / HBM_PEAK_GBS,
                           "traffic": profiled_traffic("decode_split_kernel"),
                           "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": part}
-    result["decode_breakdown_ms"] = {"page_update": pu, "partials": part, "combine": comb,
-                                     "step_events": gpu_step, "step_wall": wall * 1e3}
-    result["variant_slowdown"] = {"decode": gpu_step / var_step - 1.0 if var_step else None,
-                                  "decode_ms": {"invariant": gpu_step, "split_by_batch": var_step}}
+    result["decode_breakdown_ms"] = {"page_update": float(np.mean(pu)), "partials": part,
+                                     "combine": float(np.mean(comb)), "step_events": gpu_step,
+                                     "step_wall": wall * 1e3}
+    result["decode_stats"] = {"step_with_events": stats_ms(steps_ms), "partials": stats_ms(part_each),
+                              "page_update": stats_ms(pu), "combine": stats_ms(comb),
+                              "step_GBps_median": nb["total"] / (np.median(steps_ms) * 1e-3) / 1e9}
+    result["variant_slowdown"] = {
+        "definition": "t(invariant) / t(variant) - 1 on the same step (page update, partials, "
+                      "combine); variants pick the split count from the batch",
+        "decode_vs_2_per_cu": gpu_step / var_step - 1.0 if var_step else None,
+        "decode_vs_fill_8_per_cu": gpu_step / fill_step - 1.0 if fill_step else None,
+        "decode_ms": {"invariant": gpu_step, "split_by_batch_2_per_cu": var_step,
+                      "split_by_batch_fill_8_per_cu": fill_step}}
 
     # --- sweep over batch sizes (first B sequences of the same workload)
     sweep = []
@@ -304,16 +346,23 @@ def run_prefill_bench(args, result):
             tms[i].mark(2)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / n * 1e3
-        return (np.mean([t.ms(1, 2) for t in tms]), np.mean([t.ms(0, 2) for t in tms]), wall)
+        kern = [t.ms(1, 2) for t in tms]
+        return float(np.median(kern)), float(np.mean([t.ms(0, 2) for t in tms])), wall, kern
 
-    n = max(3, args.steps // 5)
-    kern, step_ms, wall = run(cfg, n, max(1, args.warmup // 5))
-    kern_v = None if args.profile_run else run(cfg_of(shape, bi.BI_SPLIT_BY_BATCH), n, 1)[0]
+    n = max(10, args.steps // 2)
+    kern, step_ms, wall, kern_all = run(cfg, n, max(2, args.warmup // 3))
+    kern_v = kern_f = None
+    if not args.profile_run:
+        kern_v = run(cfg_of(shape, bi.BI_SPLIT_BY_BATCH), n, 2)[0]
+        kern_f = run(cfg_of(shape, bi.BI_SPLIT_BY_BATCH_FILL), n, 2)[0]
     fl = prefill_flops(bt)
     tf = fl / (kern * 1e-3) / 1e12
+    ks = stats_ms(kern_all)
     result["prefill"] = {
         "value": fl / (max(step_ms, wall) * 1e-3) / 1e12, "unit": "TFLOP/s",
         "kernel_tflops": tf, "ms_per_step": max(step_ms, wall), "kernel_ms": kern,
+        "kernel_stats": ks,
+        "kernel_tflops_p10_p90": [fl / (ks["p90_us"] * 1e-6) / 1e12, fl / (ks["p10_us"] * 1e-6) / 1e12],
         "flops_per_step": fl,
         "config": {"workload": "prefill_bf16: 16 sequences, Hq 64, Hkv 4, D 128, cached prefix "
                                "U[0,16384], chunk U[1,2048], page 16, split 256",
@@ -321,10 +370,13 @@ def run_prefill_bench(args, result):
     }
     result["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel<bf16,128,2>",
                                   "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": tf / BF16_PEAK_TFLOPS,
+                                  "frac": tf / BF16_PEAK_TFLOPS, "kernel_ms_median": kern,
                                   "traffic": profiled_traffic("prefill_kernel")}
-    result["variant_slowdown"]["prefill"] = kern / kern_v - 1.0 if kern_v else None
-    result["variant_slowdown"]["prefill_ms"] = {"invariant": kern, "split_by_batch": kern_v}
+    vs = result.setdefault("variant_slowdown", {})
+    vs["prefill_vs_2_per_cu"] = kern / kern_v - 1.0 if kern_v else None
+    vs["prefill_vs_fill_8_per_cu"] = kern / kern_f - 1.0 if kern_f else None
+    vs["prefill_ms"] = {"invariant": kern, "split_by_batch_2_per_cu": kern_v,
+                        "split_by_batch_fill_8_per_cu": kern_f}
     run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref)
     return bt, ref
 
@@ -368,6 +420,184 @@ def run_varlen_bench(args, result, shape, bt, cfg, q, kc, vc, pt, ref):
                         "config": {"workload": "the prefill workload with dense keys and values "
                                                "[rows][Hkv][D] (bi_attn_varlen)"}}
     log(f"varlen (dense K/V): {result['varlen']['kernel_tflops']:.1f} TFLOP/s, same bits as paged")
+
+
+# ----------------------------------------------------------------------------- long decode
+def run_long_decode_bench(args, result):
+    """Long-context decode: 8 sequences of 131072 tokens, 64/4 heads, q x 4 (peaked softmax);
+    each split kernel launch reads 2.15 GB of K/V, far more than the last-level cache."""
+    shape = CONFIG_SHAPES["long_decode_bf16"]
+    cfg = cfg_of(shape)
+    L, B = 131072, 8
+    bt = build_batch(shape, [SeqSpec(i, L - 1, 1) for i in range(B)], seed=2028, page_seed=2029,
+                     q_scale=4.0)
+    log(f"long decode workload: B={B} x {L}, KV {decode_bytes(shape, bt.seq_lens)['kv'] / 1e9:.2f} GB")
+    q, kn, vn = dev(bt.q, torch.bfloat16), dev(bt.k_new, torch.bfloat16), dev(bt.v_new, torch.bfloat16)
+    kc, vc = dev(bt.k_pool, torch.bfloat16), dev(bt.v_pool, torch.bfloat16)
+    pt, sl, qs = dev(bt.page_table, torch.int32), dev(bt.seq_lens, torch.int32), dev(bt.q_starts, torch.int32)
+    ws = torch.empty(bi.bi_attn_workspace_bytes(cfg, B, L) // 4 + 64, device="cuda")
+    out = torch.empty((B, shape.num_q_heads, shape.head_dim), device="cuda")
+    bi.bi_kv_page_update(cfg, kn, vn, qs, sl, pt, kc, vc)
+    bi.bi_attn_decode(cfg, q, kc, vc, pt, sl, L, out, ws)
+    ref = out.clone()
+    for b in (0, 5):        # each sequence alone at batch size 1: the same bits
+        it = torch.tensor([b], device="cuda")
+        o1 = torch.empty((1, shape.num_q_heads, shape.head_dim), device="cuda")
+        bi.bi_attn_decode(cfg, q[it].contiguous(), kc, vc, pt[it].contiguous(), sl[it].contiguous(), L, o1, ws)
+        assert torch.equal(o1.view(torch.int32), ref[b:b + 1].view(torch.int32)), "long decode B=1 vs B=8"
+
+    def step(tm=None):
+        if tm: tm.mark(0)
+        bi.bi_kv_page_update(cfg, kn, vn, qs, sl, pt, kc, vc)
+        if tm: tm.mark(1)
+        bi.bi_attn_decode_partials(cfg, q, kc, vc, pt, sl, L, ws)
+        if tm: tm.mark(2)
+        bi.bi_attn_decode_combine(cfg, sl, L, out, ws)
+        if tm: tm.mark(3)
+
+    for _ in range(3):
+        step()
+    n = max(10, args.steps // 2)
+    whole = Timer(2)
+    torch.cuda.synchronize()
+    whole.mark(0)
+    for _ in range(n):
+        step()
+    whole.mark(1)
+    torch.cuda.synchronize()
+    step_ms = whole.ms(0, 1) / n
+    tms = [Timer(4) for _ in range(n)]
+    for t in tms:
+        step(t)
+    torch.cuda.synchronize()
+    part = [t.ms(1, 2) for t in tms]
+    nb = decode_bytes(shape, bt.seq_lens)
+    gbs = nb["split_kernel"] / (np.median(part) * 1e-3) / 1e9
+    result["long_decode"] = {
+        "value": nb["total"] / (step_ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": step_ms,
+        "step_stats": stats_ms([t.ms(0, 3) for t in tms]), "partials_stats": stats_ms(part),
+        "combine_stats": stats_ms([t.ms(2, 3) for t in tms]),
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1>", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": float(np.median(part))},
+        "invariance": "bitwise: sequences 0 and 5 alone at B=1 equal to the B=8 call",
+        "config": {"workload": "long_decode_bf16: 8 sequences x 131072 tokens, Hq 64, Hkv 4, D 128, "
+                               "q x 4, page 16 (shuffled), split 256 (512 splits folded in order)"}}
+    log(f"long decode: step {result['long_decode']['value']:.0f} GB/s, split kernel {gbs:.0f} GB/s")
+    return bt, ref
+
+
+# ----------------------------------------------------------------------------- mixed trace
+def run_trace_bench(args, result):
+    """The mixed continuous-batching trace: 256 requests, 64 steps of at most 8192 tokens, decode
+    tokens first then FCFS prompt chunks, 64/4 heads; each step is the page update, one decode
+    call for the decode tokens and one prefill call for the chunks. Inputs are generated on the
+    device for all steps before timing."""
+    from synth import mixed_trace
+    from synth.device import normal_tokens
+    from synth.workloads import PageAllocator
+    HQ, HKV, D, P = 64, 4, 128, 16
+    cfg = bi.AttnConfig(HQ, HKV, D, P, 256, bi.BI_BF16)
+    seed = 2029
+    tr = mixed_trace(seed)
+    num_pages = 48 * 1024
+    kc = torch.zeros((num_pages, HKV, P, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    alloc = PageAllocator(num_pages, seed=seed)
+    steps = []
+    for st in tr.steps:
+        dec = [(r, pos, 1) for r, pos in st.decode]
+        pre = [(r, s0, n) for r, s0, n in st.prefill]
+        ent = dec + pre
+        req = torch.tensor([r for r, s0, n in ent for _ in range(n)], device="cuda")
+        pos = torch.tensor([p for r, s0, n in ent for p in range(s0, s0 + n)], device="cuda")
+        pages = [alloc.ensure(r, s0 + n, P) for r, s0, n in ent]
+        mp = max(len(pg) for pg in pages)
+        table = torch.full((len(ent), mp), -1, dtype=torch.int32)
+        for i, pg in enumerate(pages):
+            table[i, :len(pg)] = torch.tensor(pg, dtype=torch.int32)
+        sl = [s0 + n for r, s0, n in ent]
+        qs = [0] + list(np.cumsum([n for _, _, n in ent]))
+        nd = len(dec)
+        d = {"q": normal_tokens(seed, req, "q", pos, HQ, D),
+             "kn": normal_tokens(seed, req, "k", pos, HKV, D),
+             "vn": normal_tokens(seed, req, "v", pos, HKV, D),
+             "table": table.cuda(), "sl": torch.tensor(sl, dtype=torch.int32, device="cuda"),
+             "qs": torch.tensor(qs, dtype=torch.int32, device="cuda"), "nd": nd,
+             "dec_bytes": decode_bytes(CONFIG_SHAPES["mixed_trace_bf16"], sl[:nd])["total"] if nd else 0,
+             "pre_flops": sum(4 * D * HQ * (n * (s0 + 1) + n * (n - 1) // 2) for _, s0, n in pre),
+             "pre_tokens": sum(n for _, _, n in pre)}
+        if nd:
+            d["dq"] = d["q"][:nd].contiguous()
+            d["dtable"] = d["table"][:nd].contiguous()
+            d["dsl"] = d["sl"][:nd].contiguous()
+            d["dmx"] = max(sl[:nd])
+            d["dws"] = torch.empty(bi.bi_attn_workspace_bytes(cfg, nd, d["dmx"]) // 4 + 64, device="cuda")
+            d["dout"] = torch.empty((nd, HQ, D), device="cuda")
+        if pre:
+            d["pq"] = d["q"][nd:].contiguous()
+            d["ptable"] = d["table"][nd:].contiguous()
+            d["psl"] = d["sl"][nd:].contiguous()
+            d["pqs"] = (d["qs"][nd:] - nd).contiguous()
+            d["pmxq"] = max(n for _, _, n in pre)
+            d["pmx"] = max(sl[nd:])
+            d["pout"] = torch.empty((d["pre_tokens"], HQ, D), device="cuda")
+        steps.append(d)
+        for r in st.finished:
+            alloc.release(r)
+
+    def run_step(d, tm=None):
+        if tm: tm.mark(0)
+        bi.bi_kv_page_update(cfg, d["kn"], d["vn"], d["qs"], d["sl"], d["table"], kc, vc)
+        if tm: tm.mark(1)
+        if d["nd"]:
+            bi.bi_attn_decode(cfg, d["dq"], kc, vc, d["dtable"], d["dsl"], d["dmx"], d["dout"], d["dws"])
+        if tm: tm.mark(2)
+        if "pq" in d:
+            bi.bi_attn_prefill(cfg, d["pq"], kc, vc, d["ptable"], d["pqs"], d["psl"], d["pmxq"], d["pmx"], d["pout"])
+        if tm: tm.mark(3)
+
+    # the trace once untimed (fills the cache), then timed: the steps write the same K/V again
+    for d in steps:
+        run_step(d)
+    torch.cuda.synchronize()
+    # route check on one mixed step: one prefill call with the decode tokens as 1-token chunks
+    # gives the bits of the decode call plus the prefill call
+    d = next(x for x in steps if x["nd"] and "pq" in x)
+    run_step(d)
+    T = int(d["qs"][-1])
+    o1 = torch.empty((T, HQ, D), device="cuda")
+    bi.bi_attn_prefill(cfg, d["q"], kc, vc, d["table"], d["qs"], d["sl"], max(d["pmxq"], 1),
+                       max(d["pmx"], d["dmx"]), o1)
+    assert torch.equal(o1[:d["nd"]].view(torch.int32), d["dout"].view(torch.int32)), "trace decode route"
+    assert torch.equal(o1[d["nd"]:].view(torch.int32), d["pout"].view(torch.int32)), "trace prefill route"
+    tms = [Timer(4) for _ in steps]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for d, t in zip(steps, tms):
+        run_step(d, t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [t.ms(0, 3) for t in tms]
+    dec_ms = sum(t.ms(1, 2) for t, d in zip(tms, steps) if d["nd"])
+    pre_ms = sum(t.ms(2, 3) for t, d in zip(tms, steps) if "pq" in d)
+    dec_bytes = sum(d["dec_bytes"] for d in steps)
+    pre_flops = sum(d["pre_flops"] for d in steps)
+    toks = sum(int(d["qs"][-1]) for d in steps)
+    result["mixed_trace"] = {
+        "value": toks / (sum(step_ms) * 1e-3), "unit": "tokens/s", "steps": len(steps), "tokens": toks,
+        "step_stats": stats_ms(step_ms), "wall_s": wall,
+        "decode": {"GBps": dec_bytes / (dec_ms * 1e-3) / 1e9, "ms": dec_ms, "bytes": dec_bytes},
+        "prefill": {"TFLOPs": pre_flops / (pre_ms * 1e-3) / 1e12, "ms": pre_ms, "flops": pre_flops},
+        "invariance": "bitwise: one mixed step as one prefill call (decode tokens as 1-token chunks) "
+                      "equal to its decode call plus prefill call",
+        "config": {"workload": "mixed_trace_bf16: 256 requests, 64 steps, <= 8192 tokens per step, "
+                               "prompts floor(exp U[ln 64, ln 32768]), outputs U[16, 1024], Hq 64, "
+                               "Hkv 4, D 128, page 16, split 256"}}
+    log(f"mixed trace: {toks} tokens in {sum(step_ms):.1f} ms of steps (median step "
+        f"{result['mixed_trace']['step_stats']['median_us']:.0f} us); decode "
+        f"{result['mixed_trace']['decode']['GBps']:.0f} GB/s, prefill {result['mixed_trace']['prefill']['TFLOPs']:.0f} TFLOP/s")
+    del steps, kc, vc
 
 
 # ----------------------------------------------------------------------------- RMSNorm
@@ -472,8 +702,10 @@ def run_gemm_bench(args, result):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(result, bt_dec, gpu_dec, samples):
-    """Time the fp64 oracle on the host and use its outputs for the parity check."""
+def cpu_baseline(result, bt_dec, gpu_dec, samples, pf=None, long=None):
+    """Time the fp64 oracle on the host on a bounded sample of the headline decode workload and
+    use its outputs for the parity check; also check sampled rows of the prefill and long-context
+    workloads (``pf``, ``long``: (batch, GPU output)) against the oracle."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -499,14 +731,34 @@ def cpu_baseline(result, bt_dec, gpu_dec, samples):
     parity = {"decode_rows": int(n * bt_dec.shape.num_q_heads), "max_abs": float(err.max()),
               "mean_abs": float(err.mean())}
     assert err.max() <= 2e-3 and err.mean() <= 2e-4, parity
+
+    def sampled(bt, out, rows, in_place=False):
+        kc2, vc2 = (bt.k_pool, bt.v_pool) if in_place else (bt.k_pool.copy(), bt.v_pool.copy())
+        oracle.kv_page_update(bt.k_new, bt.v_new, bt.q_starts, bt.seq_lens, bt.page_table, kc2, vc2)
+        want = oracle.paged_attention_rows(bt.q, kc2, vc2, bt.page_table, bt.q_starts, bt.seq_lens,
+                                           bt.shape.num_kv_heads, rows)
+        got = np.stack([out[t, h].double().cpu().numpy() for t, h in rows])
+        e = np.abs(got - want)
+        rec = {"rows": len(rows), "max_abs": float(e.max()), "mean_abs": float(e.mean())}
+        assert e.max() <= 2e-3 and e.mean() <= 2e-4, rec
+        return rec
+
+    if pf is not None:
+        bt_pf, out_pf = pf
+        T, Hq = bt_pf.total_tokens, bt_pf.shape.num_q_heads
+        rows = [(int(t), int(h)) for t in np.linspace(0, T - 1, 16).astype(int) for h in (0, 21, 42, Hq - 1)]
+        parity["prefill_sample"] = sampled(bt_pf, out_pf, rows)
+    if long is not None:
+        bt_l, out_l = long
+        rows = [(b, h) for b in (0, 3, 7) for h in (0, 17, 40, 63)]
+        parity["long_decode_sample"] = sampled(bt_l, out_l, rows, in_place=True)
     result["parity"] = parity
     result["cpu_baseline"] = {"value": byt / dt / 1e9, "unit": "GB/s", "cores": int(threads),
                               "kind": "oracle",
                               "sample": f"decode_bf16, first {n} of 64 sequences (all 32 heads), "
                                         f"fp64 numpy, {reps} rep(s), {dt:.2f} s each, "
                                         f"{dt * reps:.1f} s in all",
-                              "host": platform.processor() or platform.machine(),
-                              "host_cpus": os.cpu_count()}
+                              "host": host_cpu(), "host_cpus": os.cpu_count()}
 
 
 def main():
@@ -517,6 +769,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context decode workload")
+    ap.add_argument("--no-trace", action="store_true", help="skip the mixed-trace workload")
     ap.add_argument("--prefill-only", action="store_true",
                     help="measure the prefill workload alone (no headline value)")
     ap.add_argument("--cpu-samples", type=int, default=64)
@@ -567,14 +821,19 @@ def main():
     bt_dec, gpu_dec = run_decode_bench(args, result)
     log(f"decode: {result['value']:.0f} GB/s per step, split kernel "
         f"{result['roofline']['achieved']:.0f} GB/s")
+    pf = lg = None
     if not args.no_prefill:
-        run_prefill_bench(args, result)
+        pf = run_prefill_bench(args, result)
         log(f"prefill: {result['prefill']['kernel_tflops']:.1f} TFLOP/s (kernel)")
     if not args.profile_run:
+        if not args.no_long:
+            lg = run_long_decode_bench(args, result)
+        if not args.no_trace:
+            run_trace_bench(args, result)
         run_rmsnorm_bench(args, result)
         run_gemm_bench(args, result)
     if not args.no_cpu_baseline:
-        cpu_baseline(result, bt_dec, gpu_dec, args.cpu_samples)
+        cpu_baseline(result, bt_dec, gpu_dec, args.cpu_samples, pf, lg)
     print(json.dumps(result), flush=True)
 
 

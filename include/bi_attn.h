@@ -18,7 +18,7 @@
  * Conventions shared by all calls
  *  - Pointers are device pointers unless stated, 16-byte aligned, and stay owned by the
  *    caller. The library never allocates, frees or synchronises; it is stateless apart from
- *    a lazily cached CU count per device, which only affects the split-by-batch policy.
+ *    a lazily cached CU count per device, which only affects the split-by-batch policies.
  *  - Layouts (row-major, element type given by cfg->dtype unless stated):
  *      q            [T][Hq][D]                         (decode: T = batch)
  *      k_new, v_new [T][Hkv][D]
@@ -68,7 +68,10 @@ typedef enum {
   /* Comparison variant, measurement only: split size chosen per sequence from the batch size,
    * S' = roundup32(ceil(len / n)), n = clamp(ceil(2 * CUs / (batch * Hkv)), 1, ceil(len / 32)),
    * the way split-count heuristics pick their splits. Outputs change bits with the batch. */
-  BI_SPLIT_BY_BATCH = 1
+  BI_SPLIT_BY_BATCH = 1,
+  /* The same with n = clamp(ceil(8 * CUs / (batch * Hkv)), 1, ceil(len / 32)): enough splits
+   * to fill the waves the attention kernels keep resident (8 per CU). Measurement only. */
+  BI_SPLIT_BY_BATCH_FILL = 2
 } bi_split_policy;
 
 typedef struct {
@@ -102,7 +105,7 @@ int bi_kv_page_update(const bi_attn_cfg* cfg, const void* k_new, const void* v_n
  * Bytes of workspace bi_attn_decode needs for up to `rows_tokens` query tokens whose
  * sequences are at most `max_seq_len` long: per (token, q head, split) an fp32 partial
  * (max, sum of exponentials, D accumulators). bi_attn_prefill needs none. Returns 0 for an
- * invalid cfg. Host-only; queries the current device's CU count for BI_SPLIT_BY_BATCH.
+ * invalid cfg. Host-only; queries the current device's CU count for the by-batch policies.
  */
 size_t bi_attn_workspace_bytes(const bi_attn_cfg* cfg, int32_t rows_tokens, int32_t max_seq_len);
 

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     BI_BF16,
     BI_F32,
     BI_SPLIT_BY_BATCH,
+    BI_SPLIT_BY_BATCH_FILL,
     BI_SPLIT_FIXED,
     EXPORTED,
     LIB_PATH,

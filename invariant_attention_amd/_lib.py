@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbiattn.so")
 
 BI_F32, BI_BF16 = 0, 1
-BI_SPLIT_FIXED, BI_SPLIT_BY_BATCH = 0, 1
+BI_SPLIT_FIXED, BI_SPLIT_BY_BATCH, BI_SPLIT_BY_BATCH_FILL = 0, 1, 2
 BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode",

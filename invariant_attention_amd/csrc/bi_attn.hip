@@ -42,10 +42,13 @@ struct AttnParams {
 };
 
 // Split length of one sequence. Fixed policy: the configured S for every sequence and every
-// batch. By-batch policy (comparison only): derived from the batch size and the length.
+// batch. By-batch policies (comparison only): derived from the batch size and the length,
+// with a split count of about 2 per CU (BI_SPLIT_BY_BATCH) or 8 per CU, the waves the
+// attention kernels keep resident (BI_SPLIT_BY_BATCH_FILL), over the batch's KV heads.
 __device__ __forceinline__ int split_len(const AttnParams& a, int len) {
   if (a.policy == BI_SPLIT_FIXED) return a.split;
-  const int by_batch = (2 * a.num_cus + a.batch * a.hkv - 1) / (a.batch * a.hkv);
+  const int per_cu = a.policy == BI_SPLIT_BY_BATCH_FILL ? 8 : 2;
+  const int by_batch = (per_cu * a.num_cus + a.batch * a.hkv - 1) / (a.batch * a.hkv);
   const int max_n = (len + 31) / 32;
   const int n = max(1, min(by_batch, max_n));
   const int s = (len + n - 1) / n;
@@ -1108,7 +1111,9 @@ int check_cfg(const bi_attn_cfg* c) {
   if (!c) return BI_EINVAL;
   if (c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->num_q_heads % c->num_kv_heads) return BI_EINVAL;
   if (c->dtype != BI_F32 && c->dtype != BI_BF16) return BI_EINVAL;
-  if (c->split_policy != BI_SPLIT_FIXED && c->split_policy != BI_SPLIT_BY_BATCH) return BI_EINVAL;
+  if (c->split_policy != BI_SPLIT_FIXED && c->split_policy != BI_SPLIT_BY_BATCH &&
+      c->split_policy != BI_SPLIT_BY_BATCH_FILL)
+    return BI_EINVAL;
   if (!(c->softmax_scale >= 0.f) || c->softmax_scale == __builtin_inff()) return BI_EINVAL;
   if (c->split_size <= 0 || c->page_size <= 0 || c->head_dim <= 0) return BI_EINVAL;
   const int G = c->num_q_heads / c->num_kv_heads;
@@ -1127,9 +1132,11 @@ float cscale_of(const bi_attn_cfg* c) {
 int64_t jmax_of(const bi_attn_cfg* c, int64_t batch, int64_t max_seq_len) {
   if (max_seq_len <= 0) return 1;
   if (c->split_policy == BI_SPLIT_FIXED) return (max_seq_len + c->split_size - 1) / c->split_size;
-  // by-batch: at most ceil(2 CUs / (batch Hkv)) splits, and never more than ceil(len / 32)
+  // by-batch: at most ceil(k CUs / (batch Hkv)) splits (k = 2, or 8 to fill the resident
+  // waves), and never more than ceil(len / 32)
   const int64_t b = batch > 0 ? batch : 1;
-  const int64_t by_batch = (2 * (int64_t)cu_count() + b * c->num_kv_heads - 1) / (b * c->num_kv_heads);
+  const int64_t k = c->split_policy == BI_SPLIT_BY_BATCH_FILL ? 8 : 2;
+  const int64_t by_batch = (k * (int64_t)cu_count() + b * c->num_kv_heads - 1) / (b * c->num_kv_heads);
   const int64_t by_len = (max_seq_len + 31) / 32;
   return by_batch < by_len ? (by_batch > 0 ? by_batch : 1) : by_len;
 }
@@ -1150,7 +1157,7 @@ AttnParams base_params(const bi_attn_cfg* c) {
   a.split = c->split_size;
   a.policy = c->split_policy;
   a.cscale = cscale_of(c);
-  a.num_cus = c->split_policy == BI_SPLIT_BY_BATCH ? cu_count() : 0;
+  a.num_cus = c->split_policy != BI_SPLIT_FIXED ? cu_count() : 0;
   return a;
 }
 

@@ -454,21 +454,18 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
         // an all-masked row (a prefill row below the split's first key) takes the reference
         // -FLT_MAX, so its p = 2^-inf = 0 with a finite offset
         mnew[b] = mt > -3.40282347e38f ? mt : -3.40282347e38f;
-        // threshold of the peaked-split test: mean of the row's unmasked scaled scores + kGap,
-        // the lane sums in a fixed order and the row sums by the xor butterfly (every lane of
-        // the row gets the same bits); an all-masked row gets NaN, which never tests true
-        float sum = 0.f, cnt = 0.f;
+        // threshold of the peaked-split test: mean of the row's unmasked scaled scores + kGap:
+        // the lane's scores summed in a fixed order, the row sum by the xor butterfly (every
+        // lane of the row gets the same bits), divided by the unmasked count min(32, pos - key0
+        // + 1) through v_rcp_f32; an all-masked row gets 0 * inf = NaN, which never tests true
+        float sum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool in = x[b][kb][r] > -__builtin_inff();
-            sum = sum + (in ? x[b][kb][r] : 0.f);
-            cnt = cnt + (in ? 1.f : 0.f);
-          }
+          for (int r = 0; r < 4; ++r) sum = sum + (mask && !(x[b][kb][r] > -__builtin_inff()) ? 0.f : x[b][kb][r]);
         sum = xor_sum(sum);
-        cnt = xor_sum(cnt);
-        st[b].thr = (sum * cscale) / cnt + kGap;
+        const float cnt = (float)min(max(pos[b] - key0 + 1, 0), kSubTile);
+        st[b].thr = sum * cscale * __builtin_amdgcn_rcpf(cnt) + kGap;
         st[b].lo = false;
       } else {
         const bool need = mt > st[b].m + kLazy;
@@ -505,17 +502,31 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
       for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
   }
   // P_lo choice of this lane's keys (position, peaked split, outlier above the reference).
-  // The peaked flag is per row: a ballot of the lanes above the threshold, read out for the
-  // lanes c, c + 16, c + 32, c + 48 of this lane's row.
-  bool lo_row[NB];
-  bool lo_lane = false;
-  const int col = (int)(threadIdx.x & 15);
+  // The peaked flag is per row and sticky for the rest of the split: when some lane holds a
+  // scaled score above its row's threshold (rare for N(0,1)-like rows), a ballot of those
+  // lanes is read out for the lanes c, c + 16, c + 32, c + 48 of each row.
+  bool lo_row[NB], over[NB], above[NB];
+  float xm[NB];
+  unsigned long long trig = 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const float xm = mxl[b] * cscale;
-    const unsigned long long up = __builtin_amdgcn_ballot_w64(xm > st[b].thr);
-    st[b].lo = st[b].lo || ((up >> col) & 0x0001000100010001ull) != 0;
-    lo_row[b] = lo_pos[b] || st[b].lo || xm > mnew[b] + kOver;
+    xm[b] = mxl[b] * cscale;
+    above[b] = xm[b] > st[b].thr;
+    over[b] = xm[b] > mnew[b] + kOver;
+    trig |= __builtin_amdgcn_ballot_w64(above[b]);
+  }
+  if (trig != 0) {
+    const int col = (int)(threadIdx.x & 15);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const unsigned long long up = __builtin_amdgcn_ballot_w64(above[b]);
+      st[b].lo = st[b].lo || ((up >> col) & 0x0001000100010001ull) != 0;
+    }
+  }
+  bool lo_lane = false;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    lo_row[b] = lo_pos[b] || st[b].lo || over[b];
     lo_lane = lo_lane || lo_row[b];
   }
   const bool lo_any = wave_any(lo_lane);

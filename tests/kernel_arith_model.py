@@ -108,7 +108,8 @@ def attend_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray,
                         lane_cnt = (lane_cnt + fin[:, :, kb, :, r].astype(F32)).astype(F32)
                 s = _pair_sum(lane_sum)
                 n = _pair_sum(lane_cnt)
-                # threshold: mean of the scaled scores + 6 (NaN when no score is unmasked)
+                # threshold: mean of the scaled scores + 6 (NaN when no score is unmasked); the
+                # device multiplies by v_rcp_f32(n), within an ulp of the quotient used here
                 thr = ((s * c).astype(F32) / n).astype(F32)
                 thr = (thr + GAP).astype(F32)
                 lo_split = np.zeros((R, J), bool)
