@@ -126,6 +126,23 @@ int bi_attn_decode(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
                    hipStream_t stream);
 
 /*
+ * bi_attn_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and bits,
+ * with the split partials in a static device array of BI_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends; nothing is allocated or
+ * freed. Returns BI_EWORKSPACE, with nothing launched, when the call needs more than that
+ * (bi_attn_workspace_bytes-sized partials for this batch and max_seq_len; 64 MiB holds, for
+ * example, 64 sequences of up to 8192 tokens with 32 query heads). Every call on one device
+ * shares the array: calls that overlap in time on one device (different streams, host
+ * threads) race, so the caller must order them. Arguments otherwise as bi_attn_decode.
+ */
+#define BI_NOALLOC_SCRATCH_BYTES (64u << 20)
+int bi_attn_decode_noalloc(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* page_table, int32_t max_pages,
+                           int32_t num_pages, const int32_t* seq_lens, int32_t batch,
+                           int32_t max_seq_len, float* out, hipStream_t stream);
+
+/*
  * The two phases of bi_attn_decode, for callers that move or inspect the split partials
  * between them (a context-parallel decode gathers partials from several devices and folds
  * them in ascending split order on the row's owner), and for per-kernel timing.

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     bi_attn_decode,
+    bi_attn_decode_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     bi_gemm,
     bi_attn_decode_combine,
     bi_attn_decode_partials,

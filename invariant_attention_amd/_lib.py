@@ -22,7 +22,9 @@ BI_F32, BI_BF16 = 0, 1
 BI_SPLIT_FIXED, BI_SPLIT_BY_BATCH, BI_SPLIT_BY_BATCH_FILL = 0, 1, 2
 BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
 
-EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode",
+NOALLOC_SCRATCH_BYTES = 64 << 20   # BI_NOALLOC_SCRATCH_BYTES
+
+EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode", "bi_attn_decode_noalloc",
             "bi_attn_decode_partials", "bi_attn_decode_combine", "bi_attn_prefill",
             "bi_attn_varlen", "bi_status_string", "bi_rmsnorm", "bi_gemm")
 
@@ -84,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.bi_kv_page_update.argtypes = [CP, P, P, P, P, P, I, I, I, I, P, P, P]
     lib.bi_attn_decode.restype = ctypes.c_int
     lib.bi_attn_decode.argtypes = [CP, P, P, P, P, I, I, P, I, I, P, P, Z, P]
+    lib.bi_attn_decode_noalloc.restype = ctypes.c_int
+    lib.bi_attn_decode_noalloc.argtypes = [CP, P, P, P, P, I, I, P, I, I, P, P]
     lib.bi_attn_decode_partials.restype = ctypes.c_int
     lib.bi_attn_decode_partials.argtypes = [CP, P, P, P, P, I, I, P, I, I, P, Z, P]
     lib.bi_attn_decode_combine.restype = ctypes.c_int
@@ -182,6 +186,19 @@ def bi_attn_decode(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_ca
         int(max_seq_len), _ptr(out), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "bi_attn_decode")
+
+
+def bi_attn_decode_noalloc(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                           max_seq_len: int, out: torch.Tensor, stream=None) -> None:
+    """``bi_attn_decode`` with the split partials in the library's static device array (no
+    workspace, nothing allocated); calls that overlap on one device race."""
+    _check_decode(cfg, "bi_attn_decode_noalloc", q, k_cache, v_cache, page_table, seq_lens, out)
+    st = load().bi_attn_decode_noalloc(
+        ctypes.byref(cfg.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        page_table.shape[1], k_cache.shape[0], _ptr(seq_lens), seq_lens.shape[0],
+        int(max_seq_len), _ptr(out), _stream(stream))
+    _check(st, "bi_attn_decode_noalloc")
 
 
 def _check_decode(cfg: AttnConfig, w: str, q, k_cache, v_cache, page_table, seq_lens, out) -> None:

@@ -1275,6 +1275,27 @@ int launch_prefill(const AttnParams& a, hipStream_t s) {
   return launched();
 }
 
+// Allocation-free decode: the split partials live in a static device array of
+// BI_NOALLOC_SCRATCH_BYTES (each device the library runs on holds its own copy until the
+// process ends). Host code never names the array as an address: the device address is
+// queried once per device with hipGetSymbolAddress (the device current at the call) and kept.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[BI_NOALLOC_SCRATCH_BYTES];
+
+void* scratch_ptr() {
+  static void* ptrs[64];   // per device (benign race: every caller stores the same address)
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -1332,6 +1353,23 @@ int bi_attn_decode(const bi_attn_cfg* cfg, const void* q, const void* k_cache, c
   if (st != BI_OK) return st < 0 ? BI_OK : st;
   if (dispatch_partials(cfg, a, stream) != BI_OK) return BI_EHIP;
   return launch_combine(a, cfg->head_dim, stream);
+}
+
+int bi_attn_decode_noalloc(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* page_table, int32_t max_pages,
+                           int32_t num_pages, const int32_t* seq_lens, int32_t batch,
+                           int32_t max_seq_len, float* out, hipStream_t stream) {
+  const int st = check_cfg(cfg);
+  if (st != BI_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return BI_EINVAL;
+  if (batch == 0) return BI_OK;
+  if (ws_bytes(cfg, batch, batch, max_seq_len) > (size_t)BI_NOALLOC_SCRATCH_BYTES) return BI_EWORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) return BI_EHIP;
+  // every partial the combine reads is written by the partials kernel of the same call first,
+  // so nothing needs clearing between calls
+  return bi_attn_decode(cfg, q, k_cache, v_cache, page_table, max_pages, num_pages, seq_lens, batch,
+                        max_seq_len, out, ws, (size_t)BI_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int bi_attn_decode_partials(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
