@@ -294,6 +294,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   typename F::Q qf[NB];
   load_q_of(qf, u.b, true);
   RowState<D> st[NB];
+  int lo_wave = 0;   // some row of the wave has its split's peaked flag set (wave-uniform)
   bool has_next = false;
   // sub-tile t of unit u; t == u.nw is sub-tile 0 of the next unit when `next`, else (and when
   // there is none) the stand-ins
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
       else return F::pack_v(buf.v, x);      // row block x, head dim NM c + x
     };
     subtile_step<E, D, NB>(st, qf, posv, getK, getV, a.cscale, key0, g, u.w0 + t == 0,
-                                  key0 + kSubTile - 1 > pos, lov);
+                                  key0 + kSubTile - 1 > pos, lov, lo, lo_wave);
   };
   // Every sub-tile of unit u, its first one already in flight in b0. Even sub-tiles are
   // computed from b0 and odd ones from b1; the next unit's first sub-tile goes to b0, during
@@ -709,9 +710,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
   }
 
   // position part of the P_lo choice (the positions are fixed for the whole tile)
-  bool lo_c[NBW];
+  bool lo_c[NBW], lo_any_c = false;
 #pragma unroll
-  for (int cb = 0; cb < NBW; ++cb) lo_c[cb] = needs_lo(pos_c[cb]);
+  for (int cb = 0; cb < NBW; ++cb) {
+    lo_c[cb] = needs_lo(pos_c[cb]);
+    lo_any_c = lo_any_c || lo_c[cb];
+  }
+  const bool lo_w = wave_any(lo_any_c);
+  int lo_wave = 0;   // some row of the wave has its split's peaked flag set (wave-uniform)
   const int nsub = bad_seq ? 0 : (pos_max_wg + kSubTile) / kSubTile;
   // page ids of the logical pages the tile reads, in an LDS ring of kPageCache entries
   // (logical page lp in slot lp % kPageCache), refilled half a ring ahead of use
@@ -827,7 +833,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
       // all blocks advance together; on the diagonal of the tile the mask leaves rows whose
       // position is below key0 as they are (see subtile_step)
       subtile_step<E, D, NBW, BF>(st, qf, pos_c, getK, getV, a.cscale, key0, g, first,
-                                  key0 + kSubTile - 1 > wave_min, lo_c);
+                                  key0 + kSubTile - 1 > wave_min, lo_c, lo_w, lo_wave);
     }
     if (last_of_split && wave_max >= j * S) {
       // fold split j into the rows of every block that reaches it (also when this wave's rows

@@ -356,26 +356,25 @@ constexpr float kLazy = 8.0f;
 // Precision of P in the bf16 PV product. P_hi = bf16(p) alone carries a relative error up to
 // 2^-9 per key, which reaches the output in proportion to the key's share of the softmax: a
 // few keys carrying most of the weight pass it on almost whole. The P_lo term (p - P_hi, a
-// second bf16) is added for the keys of a lane when any of these holds:
+// second bf16) is added for the keys of a lane when either holds:
 //   * the row is at a position below kLoKeys (few keys, so every key's share is large);
 //   * the row's split is peaked: from the sub-tile on where some lane of the row holds a
 //     scaled score more than kGap (base-2 units) above the mean of the row's unmasked scaled
-//     scores in the split's first sub-tile, to the end of the split (N(0,1)-like rows put
-//     their largest scores about 3 above that mean and rarely pass 6, sharper softmaxes pass
-//     it within a sub-tile or two);
-//   * the lane holds a key more than 2^kOver above the reference (an outlier that the lazy
-//     reference did not absorb).
-// Each decision depends only on the row's own scores, position and state, so every route
-// takes the same one; lanes without P_lo add exact zeros.
+//     scores in the split's first sub-tile, to the end of the split. N(0,1)-like rows put
+//     their largest scores about 3 above that mean and pass 7, about 4.9 standard deviations,
+//     in about one split in 3000; sharper softmaxes pass it within a sub-tile or two, and so
+//     does a lone outlier key.
+// Each decision depends only on the row's own scores and position, so every route takes the
+// same one; lanes without P_lo add exact zeros.
 constexpr int kLoKeys = 1024;
-constexpr float kGap = 6.0f;
-constexpr float kOver = 4.0f;
+constexpr float kGap = 7.0f;
 __device__ __forceinline__ bool needs_lo(int pos) { return pos >= 0 && pos < kLoKeys; }
 
 template <int D> struct RowState {
   static constexpr int NM = D / 16;
   float m, l;
-  float thr;   // mean of the scaled scores of the split's first sub-tile + kGap (NaN: none)
+  float gate;  // raw score of the peaked-split test: (mean of the split's first sub-tile's
+               // scaled scores + kGap) / cscale (NaN when that sub-tile has no unmasked key)
   bool lo;     // the split has turned out peaked: P_lo for its keys from then on
   f32x4 acc[NM];
 };
@@ -389,8 +388,11 @@ __device__ __forceinline__ bool wave_any(bool v) { return __builtin_amdgcn_ballo
 //   pos[b]        -> this lane's row position in block b
 //   first: first sub-tile of the split (state reset, not rescaled)
 //   mask:  some key of the sub-tile may lie after some row's position (wave-uniform)
-//   lo_pos[b]: needs_lo(pos[b]) (depends on the position only, so callers compute it once);
-//          the split and outlier parts of the P_lo choice are taken here
+//   lo_pos[b]: needs_lo(pos[b]); lo_pos_w: some lane of the wave has it (wave-uniform); both
+//          depend on the positions only, so callers compute them once
+//   lo_wave: wave-uniform, nonzero when some row of the wave has its split's peaked flag set
+//          (kept by the caller from one sub-tile of the split to the next; reset here at the
+//          split's first sub-tile)
 //   A row with pos < key0 (all its keys masked) takes p = 0 everywhere, which leaves its state
 //   bitwise as it was; at a split start it gets the empty state (m = -FLT_MAX, l = 0,
 //   acc = 0), which the ascending fold leaves bitwise unchanged (a = 1, b = 0).
@@ -400,7 +402,8 @@ template <typename E, int D, int NB, bool PIPE = false, class KGet, class VGet>
 __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Frag<E, D>::Q* q,
                                              const int* pos, KGet&& getK, VGet&& getV,
                                              float cscale, int key0, int g, bool first,
-                                             bool mask, const bool (&lo_pos)[NB]) {
+                                             bool mask, const bool (&lo_pos)[NB], bool lo_pos_w,
+                                             int& lo_wave) {
   using F = Frag<E, D>;
   constexpr int NM = D / 16;
   typename F::Q qv[NB];
@@ -427,16 +430,6 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     mxl[b] = vmax(vmax3(x[b][0][0], x[b][0][1], x[b][0][2]),
                   vmax3(x[b][0][3], x[b][1][0], vmax3(x[b][1][1], x[b][1][2], x[b][1][3])));
   }
-  // A row raises its reference only if some lane of it holds a scaled score above m + kLazy
-  // (the scaled row max is the max of the lanes' scaled maxima: rounding is monotonic), so
-  // the row max butterfly runs only at a split start or when some lane of the wave needs it.
-  bool full = first;
-  if (!first) {
-    unsigned long long up = 0;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) up |= __builtin_amdgcn_ballot_w64(mxl[b] * cscale > st[b].m + kLazy);
-    full = up != 0;
-  }
   float mnew[NB], alpha[NB], lnew[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -444,39 +437,80 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
     alpha[b] = 1.0f;
   }
   bool rescale = false;
-  if (full) {
-    unsigned long long need_any = 0;
+  // Past the split's first sub-tile, a sub-tile none of whose lanes holds a raw score above
+  // its row's gate needs no decision: the gate is at least one base-2 unit below m + kLazy
+  // once scaled (m is at least the first sub-tile's max, so at least its mean), so no row
+  // raises its reference, and the peaked flag stays as it is. One compare per block.
+  unsigned long long gate_hit = 0;
+  if (!first) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) gate_hit |= __builtin_amdgcn_ballot_w64(mxl[b] > st[b].gate);
+  }
+  if (first || gate_hit != 0) {
+    // A row raises its reference only if some lane of it holds a scaled score above
+    // m + kLazy (the scaled row max is the max of the lanes' scaled maxima: rounding is
+    // monotonic), so the row max butterfly runs only at a split start or when some lane of the
+    // wave needs it.
+    bool full = first;
+    if (!first) {
+      unsigned long long up = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) up |= __builtin_amdgcn_ballot_w64(mxl[b] * cscale > st[b].m + kLazy);
+      full = up != 0;
+    }
+    if (full) {
+      unsigned long long need_any = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float rm = xor_max(mxl[b]);
+        const float mt = rm * cscale;
+        if (first) {
+          // an all-masked row (a prefill row below the split's first key) takes the reference
+          // -FLT_MAX, so its p = 2^-inf = 0 with a finite offset
+          mnew[b] = mt > -3.40282347e38f ? mt : -3.40282347e38f;
+          // gate of the peaked-split test: (mean of the row's unmasked scaled scores + kGap) /
+          // cscale: the lane's scores summed in a fixed order, the row sum by the xor butterfly
+          // (every lane of the row gets the same bits), divided by the unmasked count
+          // min(32, pos - key0 + 1) through v_rcp_f32; an all-masked row gets 0 * inf = NaN,
+          // which never tests true
+          float sum = 0.f, rcnt = 1.0f / kSubTile;
+          if (mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sum = sum + (x[b][kb][r] > -__builtin_inff() ? x[b][kb][r] : 0.f);
+            rcnt = __builtin_amdgcn_rcpf((float)min(max(pos[b] - key0 + 1, 0), kSubTile));
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sum = sum + x[b][kb][r];
+          }
+          sum = xor_sum(sum);
+          st[b].gate = (sum * cscale * rcnt + kGap) * __builtin_amdgcn_rcpf(cscale);
+          st[b].lo = false;
+        } else {
+          const bool need = mt > st[b].m + kLazy;
+          if (need) {
+            mnew[b] = mt;
+            alpha[b] = ex2(st[b].m - mt);
+          }
+          need_any |= __builtin_amdgcn_ballot_w64(need);
+        }
+      }
+      rescale = !first && need_any != 0;
+    }
+    // the split's peaked flag (per row, sticky): a ballot of the lanes above their row's gate,
+    // read out for the lanes c, c + 16, c + 32, c + 48 of each row
+    const int col = (int)(threadIdx.x & 15);
+    unsigned long long any_lo = 0;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float rm = xor_max(mxl[b]);
-      const float mt = rm * cscale;
-      if (first) {
-        // an all-masked row (a prefill row below the split's first key) takes the reference
-        // -FLT_MAX, so its p = 2^-inf = 0 with a finite offset
-        mnew[b] = mt > -3.40282347e38f ? mt : -3.40282347e38f;
-        // threshold of the peaked-split test: mean of the row's unmasked scaled scores + kGap:
-        // the lane's scores summed in a fixed order, the row sum by the xor butterfly (every
-        // lane of the row gets the same bits), divided by the unmasked count min(32, pos - key0
-        // + 1) through v_rcp_f32; an all-masked row gets 0 * inf = NaN, which never tests true
-        float sum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sum = sum + (mask && !(x[b][kb][r] > -__builtin_inff()) ? 0.f : x[b][kb][r]);
-        sum = xor_sum(sum);
-        const float cnt = (float)min(max(pos[b] - key0 + 1, 0), kSubTile);
-        st[b].thr = sum * cscale * __builtin_amdgcn_rcpf(cnt) + kGap;
-        st[b].lo = false;
-      } else {
-        const bool need = mt > st[b].m + kLazy;
-        if (need) {
-          mnew[b] = mt;
-          alpha[b] = ex2(st[b].m - mt);
-        }
-        need_any |= __builtin_amdgcn_ballot_w64(need);
-      }
+      const unsigned long long up = __builtin_amdgcn_ballot_w64(mxl[b] > st[b].gate);
+      st[b].lo = st[b].lo || ((up >> col) & 0x0001000100010001ull) != 0;
+      any_lo |= __builtin_amdgcn_ballot_w64(st[b].lo);
     }
-    rescale = !first && need_any != 0;
+    lo_wave = any_lo != 0;
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -501,35 +535,11 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 #pragma unroll
       for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
   }
-  // P_lo choice of this lane's keys (position, peaked split, outlier above the reference).
-  // The peaked flag is per row and sticky for the rest of the split: when some lane holds a
-  // scaled score above its row's threshold (rare for N(0,1)-like rows), a ballot of those
-  // lanes is read out for the lanes c, c + 16, c + 32, c + 48 of each row.
-  bool lo_row[NB], over[NB], above[NB];
-  float xm[NB];
-  unsigned long long trig = 0;
+  // P_lo choice of this lane's keys: the row's position or the split's peaked flag
+  bool lo_row[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    xm[b] = mxl[b] * cscale;
-    above[b] = xm[b] > st[b].thr;
-    over[b] = xm[b] > mnew[b] + kOver;
-    trig |= __builtin_amdgcn_ballot_w64(above[b]);
-  }
-  if (trig != 0) {
-    const int col = (int)(threadIdx.x & 15);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const unsigned long long up = __builtin_amdgcn_ballot_w64(above[b]);
-      st[b].lo = st[b].lo || ((up >> col) & 0x0001000100010001ull) != 0;
-    }
-  }
-  bool lo_lane = false;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    lo_row[b] = lo_pos[b] || st[b].lo || over[b];
-    lo_lane = lo_lane || lo_row[b];
-  }
-  const bool lo_any = wave_any(lo_lane);
+  for (int b = 0; b < NB; ++b) lo_row[b] = lo_pos[b] || st[b].lo;
+  const bool lo_any = lo_pos_w || lo_wave != 0;
   f32x4 accl[NB][NM];
 #pragma unroll
   for (int b = 0; b < NB; ++b)

@@ -18,12 +18,11 @@ term of P) can be studied over whole workloads on the CPU:
   ``M' = max(M, m), a = 2^(M - M'), b = 2^(m - M'), L = fma(l, b, L a), A = fma(acc, b, A a)``.
 
 Rules for the second bf16 term (``rule``):
-  ``"kernel"``   the rule the kernels apply: rows at positions below 1024; every key of a
-                 split from the sub-tile on where some lane of the row holds a scaled score
-                 more than 6 above the mean of the row's unmasked scaled scores in the split's
-                 first sub-tile (the split is peaked; the flag stays set for the rest of the
-                 split); the keys of a lane whose largest scaled score lies more than 4 above
-                 the reference;
+  ``"kernel"``   the rule the kernels apply: rows at positions below 1024, and every key
+                 of a split from the sub-tile on where some lane of the row holds a scaled
+                 score more than 7 above the mean of the row's unmasked scaled scores in the
+                 split's first sub-tile (the split is peaked; the flag stays set for the rest
+                 of the split);
   ``"position"`` rows at positions below 1024 only;
   ``"never"`` / ``"always"``.
 
@@ -41,8 +40,7 @@ F32 = np.float32
 NEG_MAX = F32(-3.4028234663852886e38)
 LAZY = F32(8.0)
 LO_KEYS = 1024
-GAP = F32(6.0)
-OVER = F32(4.0)
+GAP = F32(7.0)
 
 
 def _fma(a, b, c):
@@ -108,7 +106,7 @@ def attend_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray,
                         lane_cnt = (lane_cnt + fin[:, :, kb, :, r].astype(F32)).astype(F32)
                 s = _pair_sum(lane_sum)
                 n = _pair_sum(lane_cnt)
-                # threshold: mean of the scaled scores + 6 (NaN when no score is unmasked); the
+                # threshold: mean of the scaled scores + 7 (NaN when no score is unmasked); the
                 # device multiplies by v_rcp_f32(n), within an ulp of the quotient used here
                 thr = ((s * c).astype(F32) / n).astype(F32)
                 thr = (thr + GAP).astype(F32)
@@ -127,8 +125,7 @@ def attend_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray,
             # sticky peaked flag: some lane of the row above the threshold
             lo_split = lo_split | ((lane_max * c).astype(F32) > thr[:, :, None]).any(axis=2)
             if rule == "kernel":
-                over = (lane_max * c).astype(F32) > (mnew[:, :, None] + OVER).astype(F32)
-                lo_lane = lo_pos | lo_split[:, :, None] | over
+                lo_lane = lo_pos | lo_split[:, :, None]
             elif rule == "position":
                 lo_lane = lo_pos
             elif rule == "always":
