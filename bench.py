@@ -127,14 +127,18 @@ def decode_workload(seed=2026, batch=64):
 
 
 def decode_bytes(shape, lens):
-    """Algorithmic bytes of one decode step: K and V once, q in, fp32 out, the page table."""
+    """Algorithmic bytes of one decode step: K and V once (the new token's rows read from the
+    new-token arrays), the new token's K and V written to its slot, q in, fp32 out, the page
+    table. The split kernel moves all but the output."""
     D, Hq, Hkv = shape.head_dim, shape.num_q_heads, shape.num_kv_heads
     lens = np.asarray(lens, np.int64)
     kv = int((lens * Hkv * D * 2 * 2).sum())
+    slot_writes = len(lens) * Hkv * D * 2 * 2
     pages = int(((lens + 15) // 16).sum()) * 4
     q_in = len(lens) * Hq * D * 2
     out = len(lens) * Hq * D * 4
-    return dict(total=kv + pages + q_in + out, split_kernel=kv + pages + q_in, kv=kv)
+    return dict(total=kv + slot_writes + pages + q_in + out,
+                split_kernel=kv + slot_writes + pages + q_in, kv=kv)
 
 
 def run_decode_bench(args, result):
@@ -181,15 +185,19 @@ def run_decode_bench(args, result):
     ws_v = torch.empty(max(bi.bi_attn_workspace_bytes(c, B, mx) for c in (cfg_v, cfg_f)) // 4 + 64,
                        device="cuda")
 
+    # One step: the page update folded into the split kernel (bi_attn_decode_append: the new
+    # token's K/V written to its slot, split partials, combine; two launches). The per-kernel
+    # pass runs the same step as its two phases with events between them.
     def step(i, c, w, tm=None):
         kc, vc = pools[i % R]
-        if tm: tm.mark(0)
-        bi.bi_kv_page_update(c, kn, vn, qs, sl, pt, kc, vc)
-        if tm: tm.mark(1)
-        bi.bi_attn_decode_partials(c, q, kc, vc, pt, sl, mx, w)
-        if tm: tm.mark(2)
+        if tm is None:
+            bi.bi_attn_decode_append(c, q, kn, vn, kc, vc, pt, sl, mx, out, w)
+            return
+        tm.mark(0)
+        bi.bi_attn_decode_append_partials(c, q, kn, vn, kc, vc, pt, sl, mx, w)
+        tm.mark(1)
         bi.bi_attn_decode_combine(c, sl, mx, out, w)
-        if tm: tm.mark(3)
+        tm.mark(2)
 
     def whole_run(c, w):
         for i in range(args.warmup):
@@ -204,16 +212,19 @@ def run_decode_bench(args, result):
         torch.cuda.synchronize()
         return tm.ms(0, 1) / args.steps, (time.perf_counter() - t0) / args.steps
 
-    # the timed steps: nothing but the three calls per step (events only around the whole run)
+    # the step folded in one call matches the separate page update + decode bit for bit
+    step(0, cfg, ws)
+    assert torch.equal(out.view(torch.int32), ref_bits.view(torch.int32)), \
+        "decode with the folded page update differs from page update + decode"
+    # the timed steps: one call per step (events only around the whole run)
     gpu_step, wall = whole_run(cfg, ws)
-    # per-kernel breakdown in a separate pass with events between the calls
-    timers = [Timer(4) for _ in range(args.steps)]
+    # per-kernel breakdown in a separate pass with events between the two phases
+    timers = [Timer(3) for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, cfg, ws, timers[i])
     torch.cuda.synchronize()
-    pu = [t.ms(0, 1) for t in timers]
-    comb = [t.ms(2, 3) for t in timers]
-    steps_ms = [t.ms(0, 3) for t in timers]
+    comb = [t.ms(1, 2) for t in timers]
+    steps_ms = [t.ms(0, 2) for t in timers]
     # the dominant kernel alone: back-to-back launches on the same stream (rotating the pools),
     # events around each launch and around the whole run (the average excludes the records)
     tk = Timer(2)
@@ -221,7 +232,7 @@ def run_decode_bench(args, result):
     tk.mark(0)
     for i in range(args.steps):
         kc, vc = pools[i % R]
-        bi.bi_attn_decode_partials(cfg, q, kc, vc, pt, sl, mx, ws)
+        bi.bi_attn_decode_append_partials(cfg, q, kn, vn, kc, vc, pt, sl, mx, ws)
     tk.mark(1)
     torch.cuda.synchronize()
     part = tk.ms(0, 1) / args.steps
@@ -230,11 +241,21 @@ def run_decode_bench(args, result):
         kc, vc = pools[i % R]
         t1 = Timer(2)
         t1.mark(0)
-        bi.bi_attn_decode_partials(cfg, q, kc, vc, pt, sl, mx, ws)
+        bi.bi_attn_decode_append_partials(cfg, q, kn, vn, kc, vc, pt, sl, mx, ws)
         t1.mark(1)
         part_each.append(t1)
     torch.cuda.synchronize()
     part_each = [t.ms(0, 1) for t in part_each]
+    # the separate page update kernel, for reference (not part of the step)
+    tpu = Timer(2)
+    torch.cuda.synchronize()
+    tpu.mark(0)
+    for i in range(args.steps):
+        kc, vc = pools[i % R]
+        bi.bi_kv_page_update(cfg, kn, vn, qs, sl, pt, kc, vc)
+    tpu.mark(1)
+    torch.cuda.synchronize()
+    pu_alone = tpu.ms(0, 1) / args.steps
 
     # variant timing (same step shape)
     var_step = fill_step = None
@@ -252,20 +273,20 @@ def run_decode_bench(args, result):
                 "global_batch": B, "seq_len": int(np.mean(bt.seq_lens)), "parallelism": "none"},
     )
     split_gbs = nb["split_kernel"] / (part * 1e-3) / 1e9
-    result["roofline"] = {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1>",
+    result["roofline"] = {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1,append>",
                           "achieved": split_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": split_gbs / HBM_PEAK_GBS,
                           "traffic": profiled_traffic("decode_split_kernel"),
                           "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": part}
-    result["decode_breakdown_ms"] = {"page_update": float(np.mean(pu)), "partials": part,
-                                     "combine": float(np.mean(comb)), "step_events": gpu_step,
-                                     "step_wall": wall * 1e3}
-    result["decode_stats"] = {"step_with_events": stats_ms(steps_ms), "partials": stats_ms(part_each),
-                              "page_update": stats_ms(pu), "combine": stats_ms(comb),
+    result["decode_breakdown_ms"] = {"append_partials": part, "combine": float(np.mean(comb)),
+                                     "step_events": gpu_step, "step_wall": wall * 1e3,
+                                     "separate_page_update_not_in_step": pu_alone}
+    result["decode_stats"] = {"step_with_events": stats_ms(steps_ms),
+                              "append_partials": stats_ms(part_each), "combine": stats_ms(comb),
                               "step_GBps_median": nb["total"] / (np.median(steps_ms) * 1e-3) / 1e9}
     result["variant_slowdown"] = {
-        "definition": "t(invariant) / t(variant) - 1 on the same step (page update, partials, "
-                      "combine); variants pick the split count from the batch",
+        "definition": "t(invariant) / t(variant) - 1 on the same step (page update folded into "
+                      "the split kernel, combine); variants pick the split count from the batch",
         "decode_vs_2_per_cu": gpu_step / var_step - 1.0 if var_step else None,
         "decode_vs_fill_8_per_cu": gpu_step / fill_step - 1.0 if fill_step else None,
         "decode_ms": {"invariant": gpu_step, "split_by_batch_2_per_cu": var_step,
@@ -446,14 +467,16 @@ def run_long_decode_bench(args, result):
         bi.bi_attn_decode(cfg, q[it].contiguous(), kc, vc, pt[it].contiguous(), sl[it].contiguous(), L, o1, ws)
         assert torch.equal(o1.view(torch.int32), ref[b:b + 1].view(torch.int32)), "long decode B=1 vs B=8"
 
+    # the same step as the decode workload's: page update folded into the split kernel
     def step(tm=None):
-        if tm: tm.mark(0)
-        bi.bi_kv_page_update(cfg, kn, vn, qs, sl, pt, kc, vc)
-        if tm: tm.mark(1)
-        bi.bi_attn_decode_partials(cfg, q, kc, vc, pt, sl, L, ws)
-        if tm: tm.mark(2)
+        if tm is None:
+            bi.bi_attn_decode_append(cfg, q, kn, vn, kc, vc, pt, sl, L, out, ws)
+            return
+        tm.mark(0)
+        bi.bi_attn_decode_append_partials(cfg, q, kn, vn, kc, vc, pt, sl, L, ws)
+        tm.mark(1)
         bi.bi_attn_decode_combine(cfg, sl, L, out, ws)
-        if tm: tm.mark(3)
+        tm.mark(2)
 
     for _ in range(3):
         step()
@@ -466,18 +489,19 @@ def run_long_decode_bench(args, result):
     whole.mark(1)
     torch.cuda.synchronize()
     step_ms = whole.ms(0, 1) / n
-    tms = [Timer(4) for _ in range(n)]
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), "long decode: folded step"
+    tms = [Timer(3) for _ in range(n)]
     for t in tms:
         step(t)
     torch.cuda.synchronize()
-    part = [t.ms(1, 2) for t in tms]
+    part = [t.ms(0, 1) for t in tms]
     nb = decode_bytes(shape, bt.seq_lens)
     gbs = nb["split_kernel"] / (np.median(part) * 1e-3) / 1e9
     result["long_decode"] = {
         "value": nb["total"] / (step_ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": step_ms,
-        "step_stats": stats_ms([t.ms(0, 3) for t in tms]), "partials_stats": stats_ms(part),
-        "combine_stats": stats_ms([t.ms(2, 3) for t in tms]),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1>", "achieved": gbs,
+        "step_stats": stats_ms([t.ms(0, 2) for t in tms]), "append_partials_stats": stats_ms(part),
+        "combine_stats": stats_ms([t.ms(1, 2) for t in tms]),
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1,append>", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                      "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": float(np.median(part))},
         "invariance": "bitwise: sequences 0 and 5 alone at B=1 equal to the B=8 call",

@@ -163,6 +163,32 @@ int bi_attn_decode_combine(const bi_attn_cfg* cfg, const int32_t* seq_lens, int3
                            size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode step with the page update folded in: the page update of the step's one new token per
+ * sequence, then decode, in the decode's own launches (one fewer kernel per step than
+ * bi_kv_page_update followed by bi_attn_decode). k_new, v_new: [batch][Hkv][D], row b the new
+ * token of sequence b, at position seq_lens[b] - 1. The kernel that reads that position takes
+ * the token's K and V rows from k_new / v_new (the bytes its slot receives) and writes them to
+ * cache[page_table[b][pos / page_size]][kv_head][pos % page_size]. Outputs, partials and the
+ * written slots are bit-identical to bi_kv_page_update (q_starts = 0, 1, ..., batch) followed by
+ * bi_attn_decode with the same arguments (same neican.ai page and section as the page update and
+ * decode above: the step writes the page before attention reads it), except that a sequence
+ * whose length is outside [1, max_seq_len] has its slot left unwritten (its row is NaN either
+ * way). No other sequence of the batch may read a new token's slot, as with the separate calls.
+ * bi_attn_decode_append_partials is its first phase (page update and split partials), for
+ * per-kernel timing; bi_attn_decode_combine completes it. Arguments otherwise as bi_attn_decode.
+ */
+int bi_attn_decode_append(const bi_attn_cfg* cfg, const void* q, const void* k_new,
+                          const void* v_new, void* k_cache, void* v_cache,
+                          const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                          const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+int bi_attn_decode_append_partials(const bi_attn_cfg* cfg, const void* q, const void* k_new,
+                                   const void* v_new, void* k_cache, void* v_cache,
+                                   const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Chunked prefill: n_new[b] = q_starts[b+1] - q_starts[b] new tokens per sequence (any
  * number, including 0 and 1), on top of a cached prefix; q [total_tokens][Hq][D]. Attention
  * reads all keys, prefix and chunk, through the page table (liuwei.blog post, section

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     bi_attn_decode_noalloc,
     NOALLOC_SCRATCH_BYTES,
     bi_gemm,
+    bi_attn_decode_append,
+    bi_attn_decode_append_partials,
     bi_attn_decode_combine,
     bi_attn_decode_partials,
     bi_attn_prefill,

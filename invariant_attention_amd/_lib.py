@@ -25,7 +25,8 @@ BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = 0, 1, 2, 3, 4
 NOALLOC_SCRATCH_BYTES = 64 << 20   # BI_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = ("bi_kv_page_update", "bi_attn_workspace_bytes", "bi_attn_decode", "bi_attn_decode_noalloc",
-            "bi_attn_decode_partials", "bi_attn_decode_combine", "bi_attn_prefill",
+            "bi_attn_decode_partials", "bi_attn_decode_combine", "bi_attn_decode_append",
+            "bi_attn_decode_append_partials", "bi_attn_prefill",
             "bi_attn_varlen", "bi_status_string", "bi_rmsnorm", "bi_gemm")
 
 
@@ -92,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.bi_attn_decode_partials.argtypes = [CP, P, P, P, P, I, I, P, I, I, P, Z, P]
     lib.bi_attn_decode_combine.restype = ctypes.c_int
     lib.bi_attn_decode_combine.argtypes = [CP, P, I, I, P, P, Z, P]
+    lib.bi_attn_decode_append.restype = ctypes.c_int
+    lib.bi_attn_decode_append.argtypes = [CP, P, P, P, P, P, P, I, I, P, I, I, P, P, Z, P]
+    lib.bi_attn_decode_append_partials.restype = ctypes.c_int
+    lib.bi_attn_decode_append_partials.argtypes = [CP, P, P, P, P, P, P, I, I, P, I, I, P, Z, P]
     lib.bi_attn_prefill.restype = ctypes.c_int
     lib.bi_attn_prefill.argtypes = [CP, P, P, P, P, I, I, P, P, I, I, I, I, P, P, Z, P]
     lib.bi_attn_varlen.restype = ctypes.c_int
@@ -237,6 +242,47 @@ def bi_attn_decode_combine(cfg: AttnConfig, seq_lens: torch.Tensor, max_seq_len:
         ctypes.byref(cfg.c()), _ptr(seq_lens), seq_lens.shape[0], int(max_seq_len), _ptr(out),
         _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check(st, "bi_attn_decode_combine")
+
+
+def _check_append(cfg: AttnConfig, w: str, k_new, v_new, seq_lens) -> None:
+    shape = (int(seq_lens.shape[0]), cfg.num_kv_heads, cfg.head_dim)
+    _expect(k_new, w, "k_new", cfg.torch_dtype, shape)
+    _expect(v_new, w, "v_new", cfg.torch_dtype, shape)
+
+
+def bi_attn_decode_append(cfg: AttnConfig, q: torch.Tensor, k_new: torch.Tensor,
+                          v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                          out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """Decode step with the page update folded in: writes row b of ``k_new``/``v_new``
+    (``[batch][Hkv][D]``) at position ``seq_lens[b] - 1`` and attends, bit-identical to
+    ``bi_kv_page_update`` then ``bi_attn_decode``."""
+    w = "bi_attn_decode_append"
+    _check_decode(cfg, w, q, k_cache, v_cache, page_table, seq_lens, out)
+    _check_append(cfg, w, k_new, v_new, seq_lens)
+    st = load().bi_attn_decode_append(
+        ctypes.byref(cfg.c()), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(page_table), page_table.shape[1], k_cache.shape[0], _ptr(seq_lens),
+        seq_lens.shape[0], int(max_seq_len), _ptr(out), _ptr(workspace), _nbytes(workspace),
+        _stream(stream))
+    _check(st, w)
+
+
+def bi_attn_decode_append_partials(cfg: AttnConfig, q: torch.Tensor, k_new: torch.Tensor,
+                                   v_new: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, page_table: torch.Tensor,
+                                   seq_lens: torch.Tensor, max_seq_len: int,
+                                   workspace: torch.Tensor, stream=None) -> None:
+    """First phase of ``bi_attn_decode_append``: page update and split partials."""
+    w = "bi_attn_decode_append_partials"
+    _check_decode(cfg, w, q, k_cache, v_cache, page_table, seq_lens, None)
+    _check_append(cfg, w, k_new, v_new, seq_lens)
+    st = load().bi_attn_decode_append_partials(
+        ctypes.byref(cfg.c()), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(page_table), page_table.shape[1], k_cache.shape[0], _ptr(seq_lens),
+        seq_lens.shape[0], int(max_seq_len), _ptr(workspace), _nbytes(workspace),
+        _stream(stream))
+    _check(st, w)
 
 
 def bi_attn_prefill(cfg: AttnConfig, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

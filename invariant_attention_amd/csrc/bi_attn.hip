@@ -2,7 +2,8 @@
 //
 // Kernels
 //   page_update_kernel   scatter a step's new K/V rows into their pages (before attention)
-//   decode_split_kernel  one wave per (sequence, KV head, split): split partial -> workspace
+//   decode_split_kernel  one wave per (sequence, KV head, split): split partial -> workspace;
+//                        its APPEND form also writes each sequence's new token into its page
 //   combine_kernel       one wave per (token, q head): ascending fold of the partials, A / L
 //   prefill_kernel       one workgroup per (sequence, KV head, query tile): every split of
 //                        every row in registers, folded in the loop, A / L in the epilogue
@@ -32,6 +33,8 @@ struct AttnParams {
   const int32_t* seq_lens;
   const int32_t* q_starts;   // prefill only
   const int32_t* k_starts;   // dense (varlen) prefill only: first K/V row of each sequence
+  const char* k_new;         // decode with append: the new token of sequence b, [batch][Hkv][D]
+  const char* v_new;
   float* out;
   float* ws_acc;             // decode: [batch Hkv][jmax][group][D]
   float2* ws_ml;             // decode: [batch Hkv][jmax][group]  (m, l)
@@ -119,7 +122,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-template <typename E, int D, int NB>
+template <typename E, int D, int NB, bool APPEND>
 __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void decode_split_kernel(AttnParams a) {
   using F = Frag<E, D>;
   using KOp = typename F::KOp;
@@ -360,6 +363,37 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   for (;;) {
     has_next = next_unit(u, un);
     pgn = has_next ? unit_pages(un) : -1;
+    if constexpr (APPEND) {
+      // Page update of the sequence's new token (position seq_len - 1), in the unit that holds
+      // it: each lane that loads part of the token's K or V row in the unit's loop first copies
+      // exactly those bytes from k_new / v_new into the slot, so its own later loads of them
+      // (same lane, same address, in program order) see the token. No other wave reads the
+      // slot. A slot without a page is skipped (its sub-tile reads the stand-in rows). When the
+      // token is in the unit's first sub-tile, that sub-tile, loaded before the copy, is loaded
+      // again.
+      const int rel = u.seq_len - 1 - u.k_begin;          // offset in the split
+      const int nt = rel / kSubTile - u.w0;               // sub-tile of the unit
+      if (rel < split_len(a, u.seq_len) && nt >= 0 && nt < u.nw) {
+        const int nk = rel - kSubTile * (u.w0 + nt), sl = nk & 15;
+        const size_t src = ((size_t)u.b * a.hkv + kvh) * ROWB;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int page = __builtin_amdgcn_readlane(pg, (2 * nt + kb) & 63);
+          if ((nk >> 4) == kb && page >= 0) {
+            char* ks = const_cast<char*>(kbase) + (size_t)page * page_stride + (size_t)sl * ROWB;
+            char* vs = const_cast<char*>(vbase) + (size_t)page * page_stride + (size_t)sl * ROWB;
+            if (c == sl) {
+#pragma unroll
+              for (int s2 = 0; s2 < NKS; ++s2) F::store_k(ks, s2, g, F::k_op(a.k_new + src, s2, g));
+            }
+#pragma unroll
+            for (int i = 4 * kb; i < 4 * kb + 4; ++i)
+              if (F::vkey(i, g) - 16 * kb == sl) F::store_v(vs, c, F::v_row(a.v_new + src, c));
+            if (nt == 0) fetch(b0, 0, false);
+          }
+        }
+      }
+    }
     run();
     // q of the next unit, into registers the last compute no longer needs (its latency overlaps
     // the partial's stores; the next unit's first loads are already in flight)
@@ -1171,14 +1205,14 @@ int launched() { return hipGetLastError() == hipSuccess ? BI_OK : BI_EHIP; }
 
 // Decode grid: as many workgroups as the device keeps resident at once (so the static split of
 // the items over the waves is also a split over time), but no more than there can be items.
-template <typename E, int D, int NB>
+template <typename E, int D, int NB, bool APPEND>
 int launch_partials_nb(const AttnParams& a, hipStream_t s) {
   static int per_cu_cache[64];   // resident workgroups per CU, per device (benign race)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   int per_cu = (dev >= 0 && dev < 64) ? per_cu_cache[dev] : 0;
   if (per_cu <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<E, D, NB>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<E, D, NB, APPEND>, kThreads, 0) !=
             hipSuccess || per_cu <= 0)
       per_cu = 1;
     (void)hipGetLastError();
@@ -1187,15 +1221,15 @@ int launch_partials_nb(const AttnParams& a, hipStream_t s) {
   const int64_t items_max = (int64_t)a.batch * a.hkv * a.jmax;
   int64_t wgs = std::min<int64_t>((int64_t)cu_count() * per_cu, (items_max + kWaves - 1) / kWaves);
   wgs = std::max<int64_t>(wgs, (a.hkv + kWaves - 1) / kWaves);   // at least one wave per KV head
-  hipLaunchKernelGGL((decode_split_kernel<E, D, NB>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<E, D, NB, APPEND>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return launched();
 }
 
-template <typename E, int D>
+template <typename E, int D, bool APPEND>
 int launch_partials(const AttnParams& a, hipStream_t s) {
-  if (a.group <= 16) return launch_partials_nb<E, D, 1>(a, s);
-  if (a.group == 32) return launch_partials_nb<E, D, 2>(a, s);
-  return launch_partials_nb<E, D, 4>(a, s);
+  if (a.group <= 16) return launch_partials_nb<E, D, 1, APPEND>(a, s);
+  if (a.group == 32) return launch_partials_nb<E, D, 2, APPEND>(a, s);
+  return launch_partials_nb<E, D, 4, APPEND>(a, s);
 }
 
 // Lane width of the combine: up to 32 splits per row, four floats per lane and every split's
@@ -1254,10 +1288,21 @@ int decode_params(const bi_attn_cfg* cfg, const void* q, const void* k_cache, co
   return BI_OK;
 }
 
+template <bool APPEND>
 int dispatch_partials(const bi_attn_cfg* cfg, const AttnParams& a, hipStream_t s) {
   const bool bf = cfg->dtype == BI_BF16;
-  if (cfg->head_dim == 128) return bf ? launch_partials<__bf16, 128>(a, s) : launch_partials<float, 128>(a, s);
-  return bf ? launch_partials<__bf16, 64>(a, s) : launch_partials<float, 64>(a, s);
+  if (cfg->head_dim == 128)
+    return bf ? launch_partials<__bf16, 128, APPEND>(a, s) : launch_partials<float, 128, APPEND>(a, s);
+  return bf ? launch_partials<__bf16, 64, APPEND>(a, s) : launch_partials<float, 64, APPEND>(a, s);
+}
+
+// Validates the new-token arguments of an appending decode and adds them to the parameters.
+int append_params(const bi_attn_cfg* cfg, const void* k_new, const void* v_new, AttnParams* a) {
+  (void)cfg;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return BI_EINVAL;
+  a->k_new = (const char*)k_new;
+  a->v_new = (const char*)v_new;
+  return BI_OK;
 }
 
 // bf16: two workgroups of 4 waves per CU (their barriers are independent, so one fills the
@@ -1357,7 +1402,7 @@ int bi_attn_decode(const bi_attn_cfg* cfg, const void* q, const void* k_cache, c
   const int st = decode_params(cfg, q, k_cache, v_cache, page_table, max_pages, num_pages, seq_lens,
                                batch, max_seq_len, out, workspace, workspace_bytes, true, true, &a);
   if (st != BI_OK) return st < 0 ? BI_OK : st;
-  if (dispatch_partials(cfg, a, stream) != BI_OK) return BI_EHIP;
+  if (dispatch_partials<false>(cfg, a, stream) != BI_OK) return BI_EHIP;
   return launch_combine(a, cfg->head_dim, stream);
 }
 
@@ -1387,7 +1432,34 @@ int bi_attn_decode_partials(const bi_attn_cfg* cfg, const void* q, const void* k
   const int st = decode_params(cfg, q, k_cache, v_cache, page_table, max_pages, num_pages, seq_lens,
                                batch, max_seq_len, nullptr, workspace, workspace_bytes, true, false, &a);
   if (st != BI_OK) return st < 0 ? BI_OK : st;
-  return dispatch_partials(cfg, a, stream);
+  return dispatch_partials<false>(cfg, a, stream);
+}
+
+int bi_attn_decode_append_partials(const bi_attn_cfg* cfg, const void* q, const void* k_new,
+                                   const void* v_new, void* k_cache, void* v_cache,
+                                   const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AttnParams a;
+  int st = decode_params(cfg, q, k_cache, v_cache, page_table, max_pages, num_pages, seq_lens,
+                         batch, max_seq_len, nullptr, workspace, workspace_bytes, true, false, &a);
+  if (st != BI_OK) return st < 0 ? BI_OK : st;
+  if ((st = append_params(cfg, k_new, v_new, &a)) != BI_OK) return st;
+  return dispatch_partials<true>(cfg, a, stream);
+}
+
+int bi_attn_decode_append(const bi_attn_cfg* cfg, const void* q, const void* k_new,
+                          const void* v_new, void* k_cache, void* v_cache,
+                          const int32_t* page_table, int32_t max_pages, int32_t num_pages,
+                          const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AttnParams a;
+  int st = decode_params(cfg, q, k_cache, v_cache, page_table, max_pages, num_pages, seq_lens,
+                         batch, max_seq_len, out, workspace, workspace_bytes, true, true, &a);
+  if (st != BI_OK) return st < 0 ? BI_OK : st;
+  if ((st = append_params(cfg, k_new, v_new, &a)) != BI_OK) return st;
+  if (dispatch_partials<true>(cfg, a, stream) != BI_OK) return BI_EHIP;
+  return launch_combine(a, cfg->head_dim, stream);
 }
 
 int bi_attn_decode_combine(const bi_attn_cfg* cfg, const int32_t* seq_lens, int32_t batch,

@@ -128,6 +128,9 @@ template <int D> struct Frag<__bf16, D> {
   __device__ static inline KOp zero_k() { return u32x4{0, 0, 0, 0}; }
   // raw V chunk of lane column c from a V row
   __device__ static inline VRow v_row(const char* row, int c) { return *(const VRow*)(row + NM * c * 2); }
+  // the inverses of k_op and v_row: a lane's part of a K or V row back to memory
+  __device__ static inline void store_k(char* row, int st, int g, KOp x) { *(u32x4*)(row + (32 * st + 8 * g) * 2) = x; }
+  __device__ static inline void store_v(char* row, int c, VRow x) { *(VRow*)(row + NM * c * 2) = x; }
   __device__ static inline VRow zero_v() { return VRow{}; }
   __device__ static inline void load_q(Q& q, const char* row, int g) {
 #pragma unroll
@@ -295,6 +298,12 @@ template <int D> struct Frag<float, D> {
       r.v[4 * s] = t[0]; r.v[4 * s + 1] = t[1]; r.v[4 * s + 2] = t[2]; r.v[4 * s + 3] = t[3];
     }
     return r;
+  }
+  __device__ static inline void store_k(char* row, int st, int g, KOp x) { *(float*)(row + (NKS * g + st) * 4) = x; }
+  __device__ static inline void store_v(char* row, int c, const VRow& x) {
+    f32x4* p = (f32x4*)(row + NM * c * 4);
+#pragma unroll
+    for (int s = 0; s < NM / 4; ++s) p[s] = f32x4{x.v[4 * s], x.v[4 * s + 1], x.v[4 * s + 2], x.v[4 * s + 3]};
   }
   __device__ static inline VRow zero_v() {
     VRow r;
