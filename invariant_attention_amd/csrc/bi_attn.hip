@@ -78,6 +78,13 @@ __device__ __forceinline__ int page_of_nb(const AttnParams& a, int b, int lp, in
   return (ok && p >= 0 && p < a.num_pages) ? p : -1;
 }
 
+// Entry i of a read-only int array through the scalar data cache (i made wave-uniform): the
+// load waits on the scalar counter only, so the vector loads in flight are not waited for.
+__device__ __forceinline__ int scalar_load_i32(const int32_t* p, int i) {
+  const __attribute__((address_space(4))) int32_t* cp = (const __attribute__((address_space(4))) int32_t*)p;
+  return cp[__builtin_amdgcn_readfirstlane(i)];
+}
+
 // Rows read in place of a page that must not be dereferenced (table entry absent, outside the
 // pool, or past the sequence end). K rows are NaN, so a query row whose causal window needs the
 // page comes out NaN while masked keys ignore them; V rows are zero, so a zero probability
@@ -101,13 +108,12 @@ __device__ __forceinline__ const char* kv_row(const char* cache, const AttnParam
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode. The work items of a KV head are the splits (b, j) of every sequence (every split but
-// the last first, then the last splits). The grid holds as many waves as the device keeps
-// resident; of W waves per head,
-// wave w takes items w, w + W, w + 2W, ..., so every resident wave (and so every CU) gets the
-// same share of the work, within one item, and no workgroup exits at once. Per item, operands
-// stream from HBM straight into MFMA registers with two sub-tiles in flight: the loads of
-// sub-tile t+1 are issued before sub-tile t is computed.
+// Decode. The work items are the splits (b, j) of every sequence, for every KV head (every
+// split but the last first, then the last splits). The grid holds as many workgroups as the
+// device keeps resident; each owns an equal strided share of the items (so every CU gets the
+// same share, within one item), and its waves take the share's items one at a time as they
+// finish the previous one. Per item, operands stream from HBM straight into MFMA registers with
+// two sub-tiles in flight: the loads of sub-tile t+1 are issued before sub-tile t is computed.
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -122,9 +128,16 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// Waves per decode workgroup: 8 (two per SIMD, one workgroup per CU) for the bf16 kernel with one
+// column block, whose 256 VGPRs allow two waves per SIMD; else 4 (one per SIMD).
+template <typename E, int NB> struct DecWaves {
+  static constexpr int value = (sizeof(E) == 2 && NB == 1) ? 8 : 4;
+};
+
 template <typename E, int D, int NB, bool APPEND>
-__global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void decode_split_kernel(AttnParams a) {
+__global__ __launch_bounds__((64 * DecWaves<E, NB>::value), 1) void decode_split_kernel(AttnParams a) {
   using F = Frag<E, D>;
+  constexpr int NWV = DecWaves<E, NB>::value;
   using KOp = typename F::KOp;
   using VRow = typename F::VRow;
   constexpr int NKS = F::NKS;
@@ -132,10 +145,27 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   constexpr int ROWB = F::ROWB;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
-  const int W = (int)(gridDim.x * kWaves) / a.hkv;             // waves per KV head
-  if (gw >= W * a.hkv) return;
-  const int kvh = gw % a.hkv, w = gw / a.hkv;
+  // Work items are the pairs I = i Hkv + h of split item i (below) and KV head h. Workgroup k
+  // owns I = k, k + G, k + 2G, ... (G workgroups), and its waves take the next of those from a
+  // counter in LDS whenever they need one: the two waves that share a SIMD do not progress at
+  // the same rate (issue arbitration favours the older one), so a fixed share per wave would
+  // leave the faster ones idle at the end. Which wave computes a split does not change its bits.
+  __shared__ int lds_next;
+  // per wave: one split's accumulators [NB 16 rows][D], staged for contiguous stores (only
+  // this wave touches its slice, and one wave's LDS accesses complete in order)
+  __shared__ __attribute__((aligned(16))) float lds_part_all[NWV][NB * 16 * D];
+  float* lds_part = lds_part_all[__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))];
+  // the first 64 sequence lengths, for the last-split lookup of a batch of up to 64 (LDS reads
+  // wait on their own counter, so that lookup never waits for the K/V loads in flight)
+  __shared__ int lds_len[64];
+  if (threadIdx.x < 64) lds_len[threadIdx.x] = (int)threadIdx.x < a.batch ? a.seq_lens[threadIdx.x] : 0;
+  if (threadIdx.x == 0) lds_next = 0;
+  __syncthreads();
+  auto claim = [&]() {
+    int n = 0;
+    if (lane == 0) n = atomicAdd(&lds_next, 1);
+    return (int)blockIdx.x + __builtin_amdgcn_readfirstlane(n) * (int)gridDim.x;
+  };
 
   // Sequences are read 64 at a time, one per lane: length and split count (0 when the length
   // is out of range; the combine writes NaN for such a row).
@@ -157,7 +187,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   }
   total_full = __builtin_amdgcn_readfirstlane(total_full);
   const int total = total_full + __builtin_amdgcn_readfirstlane(total_last);
-  if (w >= total) return;
+  const int n_items = total * a.hkv;
+  const int I0 = claim();
+  if (I0 >= n_items) return;
   // Item i -> (sequence, split, length) for increasing i: one cursor per run over the chunks
   // of 64 sequences (inclusive prefix sums of the run's per-sequence item counts in incl;
   // `before` items of the run precede the chunk).
@@ -179,7 +211,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
     return nb;
   };
   // With a fixed split size the last run is ordered by the last split's sub-tile count,
-  // largest first (ties by sequence): the waves that get one item more get the cheapest.
+  // largest first (ties by sequence), so the items taken last, at the end of the run, are the
+  // cheapest.
   const bool by_cost = a.policy == BI_SPLIT_FIXED;
   const int cmax = (a.split + kSubTile - 1) / kSubTile;
   auto last_cost = [&](int len) {
@@ -188,6 +221,22 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   };
   // sequence of the k-th last split in (cost descending, sequence) order
   auto last_by_cost = [&](int k) {
+    if (a.batch <= 64) {   // one chunk, from LDS (lane id behind an empty asm, as below)
+      int lid = lane;
+      asm volatile("" : "+v"(lid));
+      const int cost = last_cost(lds_len[lid]);
+      for (int cst = cmax; cst >= 1; --cst) {
+        unsigned long long m = __builtin_amdgcn_ballot_w64(cost == cst);
+        const int n = __builtin_popcountll(m);
+        if (k >= n) {
+          k -= n;
+          continue;
+        }
+        for (int t = 0; t < k; ++t) m &= m - 1;   // drop the k lowest set lanes
+        return (int)__builtin_ctzll(m);
+      }
+      return 0;   // not reached: k < total_last
+    }
     for (int cst = cmax; cst >= 1; --cst) {
       int cnt = 0;
       for (int cb = 0; cb < a.batch; cb += 64) cnt += wave_sum_i(last_cost(chunk_len(cb)) == cst ? 1 : 0);
@@ -214,7 +263,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
       const int nb = seek(0, i, cb0, before0, incl0);
       ob = cb0 + nb;
       oj = i - before0 - (nb > 0 ? __builtin_amdgcn_readlane(incl0, nb - 1) : 0);
-      olen = a.seq_lens[ob];   // uniform: a scalar load, which leaves the vector loads in flight
+      olen = scalar_load_i32(a.seq_lens, ob);
     } else {
       if (by_cost) {
         ob = __builtin_amdgcn_readfirstlane(last_by_cost(i - total_full));
@@ -222,17 +271,15 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
         const int nb = seek(1, i - total_full, cb1, before1, incl1);
         ob = cb1 + nb;
       }
-      olen = a.seq_lens[ob];
+      olen = scalar_load_i32(a.seq_lens, ob);
       oj = splits_of(olen) - 1;
     }
   };
-  int item = w, b = 0, j = 0, len0 = 0;
-  locate(item, b, j, len0);
+  int b = 0, j = 0, len0 = 0;
+  locate(I0 / a.hkv, b, j, len0);
 
   const size_t head_stride = (size_t)kPage * ROWB;
   const size_t page_stride = (size_t)a.hkv * head_stride;
-  const char* kbase = a.k_cache + kvh * head_stride;
-  const char* vbase = a.v_cache + kvh * head_stride;
   // Every load below is unconditional: absent pages read kNanRows / kZeroRows and heads past
   // the group read zero q, so no branch separates a buffer's loads from their use, and the
   // loads of the next sub-tile stay in flight while the current one is computed.
@@ -243,12 +290,13 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   // The loads of a unit's first sub-tile are issued while the previous unit's last sub-tile is
   // computed, so the stream of loads does not stop between splits.
   struct Unit {
-    int b, j, w0, seq_len, k_begin, nsub, nw;
+    int b, j, kvh, w0, seq_len, k_begin, nsub, nw;
   };
-  auto make_unit = [&](int ub, int uj, int w0, int len) {
+  auto make_unit = [&](int ub, int uj, int ukvh, int w0, int len) {
     Unit u;
     u.b = ub;
     u.j = uj;
+    u.kvh = ukvh;
     u.w0 = w0;
     u.seq_len = len;
     const int S = split_len(a, len);
@@ -260,27 +308,41 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   // the unit after u: the next window of its split, else window 0 of the wave's next item
   auto next_unit = [&](const Unit& u, Unit& un) {
     if (u.w0 + 32 < u.nsub) {
-      un = make_unit(u.b, u.j, u.w0 + 32, u.seq_len);
+      un = make_unit(u.b, u.j, u.kvh, u.w0 + 32, u.seq_len);
       return true;
     }
-    if (item + W >= total) return false;
-    item += W;
+    const int I = claim();
+    if (I >= n_items) return false;
     int nb2, nj2, len2;
-    locate(item, nb2, nj2, len2);
-    un = make_unit(nb2, nj2, 0, len2);
+    locate(I / a.hkv, nb2, nj2, len2);
+    un = make_unit(nb2, nj2, I % a.hkv, 0, len2);
     return true;
   };
-  auto unit_pages = [&](const Unit& u) {
-    return page_of_nb(a, u.b, u.k_begin / kPage + 2 * u.w0 + lane, u.seq_len);
+  // Page ids of a unit's window, one logical page per lane: the raw table entry (an index that
+  // must not be read is replaced by entry 0 of the row, which exists) and a ballot of the lanes
+  // whose logical page may be read; an entry is checked against the pool when it is taken, so
+  // nothing waits for the table load before the sub-tile that needs it.
+  auto unit_pages = [&](const Unit& u, unsigned long long& okm) {
+    const int lp = u.k_begin / kPage + 2 * u.w0 + lane;
+    const bool ok = lp < a.max_pages && lp * kPage < u.seq_len;
+    okm = __builtin_amdgcn_ballot_w64(ok);
+    return a.page_table[(size_t)u.b * a.max_pages + (ok ? lp : 0)];
   };
-  auto load_q_of = [&](typename F::Q (&qq)[NB], int qb, bool real) {
+  auto page_at = [&](int raw, unsigned long long okm, int i) {
+    const int p = __builtin_amdgcn_readlane(raw, i);
+    return ((okm >> i) & 1) && p >= 0 && p < a.num_pages ? p : -1;
+  };
+  // (the lane's part of the address is formed here from the lane id behind an empty asm, so it
+  // is not hoisted into a register kept, and spilled, across the loop)
+  auto load_q_of = [&](typename F::Q (&qq)[NB], int qb, int kvh, bool real) {
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const char* qbase = a.q + ((size_t)qb * a.hq + kvh * a.group) * (size_t)ROWB;
 #pragma unroll
     for (int cq = 0; cq < NB; ++cq) {
-      const int hl = cq * 16 + c;   // head within the group
-      const char* row = real && hl < a.group
-                            ? a.q + ((size_t)qb * a.hq + kvh * a.group + hl) * (size_t)ROWB
-                            : zero_rows;
-      F::load_q(qq[cq], row, g);
+      const int hl = cq * 16 + (lid & 15);   // head within the group
+      const char* row = real && hl < a.group ? qbase + (unsigned)(hl * ROWB) : zero_rows;
+      F::load_q(qq[cq], row, lid >> 4);
     }
   };
 
@@ -288,14 +350,16 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
     KOp k[2][NKS];
     VRow v[8];
   };
-  // per wave: one split's accumulators [NB 16 rows][D], staged for contiguous stores (only
-  // this wave touches its slice, and one wave's LDS accesses complete in order)
-  __shared__ __attribute__((aligned(16))) float lds_part_all[kWaves][NB * 16 * D];
-  float* lds_part = lds_part_all[threadIdx.x >> 6];
-  Unit u = make_unit(b, j, 0, len0), un;
-  int pg = unit_pages(u), pgn = -1;
+  Unit u = make_unit(b, j, I0 % a.hkv, 0, len0), un;
+  unsigned long long pgm = 0, pgmn = 0;
+  int pg = unit_pages(u, pgm), pgn = 0;
   typename F::Q qf[NB];
-  load_q_of(qf, u.b, true);
+  load_q_of(qf, u.b, u.kvh, true);
+  // K and V bases of the current unit's KV head and of the next unit's
+  const char* kbase = a.k_cache + u.kvh * head_stride;
+  const char* vbase = a.v_cache + u.kvh * head_stride;
+  const char* kbase_n = kbase;
+  const char* vbase_n = vbase;
   RowState<D> st[NB];
   int lo_wave = 0;   // some row of the wave has its split's peaked flag set (wave-uniform)
   bool has_next = false;
@@ -304,11 +368,10 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   auto fetch = [&](Buf& buf, int t, bool next) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int pc = __builtin_amdgcn_readlane(pg, (2 * t + kb) & 63);
-      const int pn = __builtin_amdgcn_readlane(pgn, kb);
-      const int page = t < u.nw ? pc : (next && has_next ? pn : -1);
-      const char* kp = page >= 0 ? kbase + (size_t)page * page_stride : nan_rows;
-      const char* vp = page >= 0 ? vbase + (size_t)page * page_stride : zero_rows;
+      const int page = t < u.nw ? page_at(pg, pgm, (2 * t + kb) & 63)
+                                : (next && has_next ? page_at(pgn, pgmn, kb) : -1);
+      const char* kp = page >= 0 ? (t < u.nw ? kbase : kbase_n) + (size_t)page * page_stride : nan_rows;
+      const char* vp = page >= 0 ? (t < u.nw ? vbase : vbase_n) + (size_t)page * page_stride : zero_rows;
 #pragma unroll
       for (int s2 = 0; s2 < NKS; ++s2) buf.k[kb][s2] = F::k_op(kp + c * ROWB, s2, g);
 #pragma unroll
@@ -362,7 +425,11 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
   fetch(b0, 0, false);
   for (;;) {
     has_next = next_unit(u, un);
-    pgn = has_next ? unit_pages(un) : -1;
+    if (has_next) pgn = unit_pages(un, pgmn);
+    if (has_next) {
+      kbase_n = a.k_cache + un.kvh * head_stride;
+      vbase_n = a.v_cache + un.kvh * head_stride;
+    }
     if constexpr (APPEND) {
       // Page update of the sequence's new token (position seq_len - 1), in the unit that holds
       // it: each lane that loads part of the token's K or V row in the unit's loop first copies
@@ -375,10 +442,10 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
       const int nt = rel / kSubTile - u.w0;               // sub-tile of the unit
       if (rel < split_len(a, u.seq_len) && nt >= 0 && nt < u.nw) {
         const int nk = rel - kSubTile * (u.w0 + nt), sl = nk & 15;
-        const size_t src = ((size_t)u.b * a.hkv + kvh) * ROWB;
+        const size_t src = ((size_t)u.b * a.hkv + u.kvh) * ROWB;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int page = __builtin_amdgcn_readlane(pg, (2 * nt + kb) & 63);
+          const int page = page_at(pg, pgm, (2 * nt + kb) & 63);
           if ((nk >> 4) == kb && page >= 0) {
             char* ks = const_cast<char*>(kbase) + (size_t)page * page_stride + (size_t)sl * ROWB;
             char* vs = const_cast<char*>(vbase) + (size_t)page * page_stride + (size_t)sl * ROWB;
@@ -397,31 +464,40 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && NB == 1) ? 2 : 1) void
     run();
     // q of the next unit, into registers the last compute no longer needs (its latency overlaps
     // the partial's stores; the next unit's first loads are already in flight)
-    if (has_next && un.b != u.b) load_q_of(qf, un.b, true);
+    if (has_next && (un.b != u.b || un.kvh != u.kvh)) load_q_of(qf, un.b, un.kvh, true);
     if (u.w0 + u.nw >= u.nsub) {
       // Partial of split u.j: the accumulators of the group's heads are one contiguous block
       // of the workspace, written through the wave's LDS slice in whole 1 KB stores (each lane
-      // holds 4 NM scattered-by-row values; stored directly they would be 16-byte pieces).
+      // holds 4 NM scattered-by-row values; stored directly they would be 16-byte pieces). The
+      // lane's addresses are formed here from the lane id behind an empty asm: hoisted, they
+      // would be registers kept (and spilled) across the loop, and a reload waits for every load
+      // in flight.
+      int lid = lane;
+      asm volatile("" : "+v"(lid));
 #pragma unroll
       for (int cq = 0; cq < NB; ++cq) {
-        float* lrow = lds_part + (cq * 16 + c) * D + 4 * g * NM;
+        const int hl = cq * 16 + (lid & 15);
+        float* lrow = lds_part + hl * D + 4 * (lid >> 4) * NM;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int mb = 0; mb < NM; mb += 4)
             *(f32x4*)(lrow + r * NM + mb) = f32x4{st[cq].acc[mb][r], st[cq].acc[mb + 1][r],
                                                   st[cq].acc[mb + 2][r], st[cq].acc[mb + 3][r]};
-        const int hl = cq * 16 + c;
         const float rl = row_l(st[cq]);
-        if (g == 0 && hl < a.group)
-          a.ws_ml[part_index(a, (size_t)u.b * a.hq + kvh * a.group + hl, u.j)] = make_float2(st[cq].m, rl);
+        if ((lid >> 4) == 0 && hl < a.group)
+          a.ws_ml[part_index(a, (size_t)u.b * a.hq + u.kvh * a.group + hl, u.j)] = make_float2(st[cq].m, rl);
       }
-      float* dst = a.ws_acc + part_index(a, (size_t)u.b * a.hq + kvh * a.group, u.j) * D;
-      for (int i = lane; i < a.group * (D / 4); i += 64) *(f32x4*)(dst + 4 * i) = *(const f32x4*)(lds_part + 4 * i);
+      char* dst = (char*)(a.ws_acc + part_index(a, (size_t)u.b * a.hq + u.kvh * a.group, u.j) * D);
+      for (int i = lid; i < a.group * (D / 4); i += 64)
+        *(f32x4*)(dst + (unsigned)i * 16u) = *(const f32x4*)(lds_part + 4 * i);
     }
     if (!has_next) break;
     u = un;
     pg = pgn;
+    pgm = pgmn;
+    kbase = kbase_n;
+    vbase = vbase_n;
   }
 }
 
@@ -1207,21 +1283,22 @@ int launched() { return hipGetLastError() == hipSuccess ? BI_OK : BI_EHIP; }
 // the items over the waves is also a split over time), but no more than there can be items.
 template <typename E, int D, int NB, bool APPEND>
 int launch_partials_nb(const AttnParams& a, hipStream_t s) {
+  constexpr int NWV = DecWaves<E, NB>::value;
   static int per_cu_cache[64];   // resident workgroups per CU, per device (benign race)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   int per_cu = (dev >= 0 && dev < 64) ? per_cu_cache[dev] : 0;
   if (per_cu <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<E, D, NB, APPEND>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<E, D, NB, APPEND>, 64 * NWV, 0) !=
             hipSuccess || per_cu <= 0)
       per_cu = 1;
     (void)hipGetLastError();
     if (dev >= 0 && dev < 64) per_cu_cache[dev] = per_cu;
   }
   const int64_t items_max = (int64_t)a.batch * a.hkv * a.jmax;
-  int64_t wgs = std::min<int64_t>((int64_t)cu_count() * per_cu, (items_max + kWaves - 1) / kWaves);
-  wgs = std::max<int64_t>(wgs, (a.hkv + kWaves - 1) / kWaves);   // at least one wave per KV head
-  hipLaunchKernelGGL((decode_split_kernel<E, D, NB, APPEND>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+  int64_t wgs = std::min<int64_t>((int64_t)cu_count() * per_cu, (items_max + NWV - 1) / NWV);
+  wgs = std::max<int64_t>(wgs, 1);
+  hipLaunchKernelGGL((decode_split_kernel<E, D, NB, APPEND>), dim3((unsigned)wgs), dim3(64 * NWV), 0, s, a);
   return launched();
 }
 
