@@ -1279,8 +1279,8 @@ AttnParams base_params(const bi_attn_cfg* c) {
 
 int launched() { return hipGetLastError() == hipSuccess ? BI_OK : BI_EHIP; }
 
-// Decode grid: as many workgroups as the device keeps resident at once (so the static split of
-// the items over the waves is also a split over time), but no more than there can be items.
+// Decode grid: as many workgroups as the device keeps resident at once, but no more than there
+// can be items.
 template <typename E, int D, int NB, bool APPEND>
 int launch_partials_nb(const AttnParams& a, hipStream_t s) {
   constexpr int NWV = DecWaves<E, NB>::value;
@@ -1295,8 +1295,10 @@ int launch_partials_nb(const AttnParams& a, hipStream_t s) {
     (void)hipGetLastError();
     if (dev >= 0 && dev < 64) per_cu_cache[dev] = per_cu;
   }
+  // up to one workgroup per item: a small batch spreads over as many CUs as it has items (one
+  // CU's own bandwidth is the limit there), a large one fills every resident slot
   const int64_t items_max = (int64_t)a.batch * a.hkv * a.jmax;
-  int64_t wgs = std::min<int64_t>((int64_t)cu_count() * per_cu, (items_max + NWV - 1) / NWV);
+  int64_t wgs = std::min<int64_t>((int64_t)cu_count() * per_cu, items_max);
   wgs = std::max<int64_t>(wgs, 1);
   hipLaunchKernelGGL((decode_split_kernel<E, D, NB, APPEND>), dim3((unsigned)wgs), dim3(64 * NWV), 0, s, a);
   return launched();
