@@ -7,7 +7,7 @@ decode, chunked-prefill, long-context (q x 4) and mixed-trace workloads, eight s
 peaked rows at 1024-4096 keys and a sweep of softmax sharpness, against the float64
 definition. The rule must keep every case within max-abs 1e-3 (half the parity bar of 2e-3) and
 mean-abs 1e-4. The position-only rule that the kernels used before is shown to miss the bar on
-peaked rows, which is what the per-split and outlier parts of the rule are for.
+peaked rows, which is what the per-split (peaked-split) part of the rule is for.
 """
 
 from __future__ import annotations
@@ -122,8 +122,8 @@ def test_position_only_rule_misses_peaked_rows():
 
 def test_rule_adds_little_for_unpeaked_long_rows():
     # N(0,1) rows past position 1024 (the prefill and trace workloads' bulk): the second bf16
-    # term is rare (a split whose scores pass the first sub-tile's mean by 6, about 4.2 standard
-    # deviations, or an outlier lane), so the rule costs those rows almost nothing
+    # term is rare (a split with a score more than 7 above the first sub-tile's mean, about 4.9
+    # standard deviations), so the rule costs those rows almost nothing
     st = {}
     q, K, V, pos = _rows(3700, 16384, np.arange(1024, 16384, 61), 16)
     attend_rows(q, K, V, pos, rule="kernel", stats=st)
