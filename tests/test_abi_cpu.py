@@ -163,6 +163,14 @@ def test_bindings_refuse_wrong_dtypes_and_shapes():
         bi.bi_kv_page_update(cfg, a["kn"], a["kn"] if "kn" in kw else a["kn"].clone(), a["qs"],
                              a["sl"], a["pt"], a["kc"], a["vc"])
 
+    def append(**kw):
+        a = {**good(), **kw}
+        q = a["q"][:B] if "q" not in kw else a["q"]
+        out = a["out"][:B] if "out" not in kw else a["out"]
+        kn = a["kn"][:B] if "kn" not in kw else a["kn"]
+        bi.bi_attn_decode_append(cfg, q, kn, kn.clone(), a["kc"], a["vc"], a["pt"], a["sl"], 64, out,
+                                 torch.zeros(8))
+
     bad_cases = [
         (prefill, dict(q=torch.zeros((T, 64, 128), dtype=f32)), "q must be"),           # fp32 q, bf16 cfg
         (prefill, dict(out=torch.zeros((T, 64, 128), dtype=bf)), "out must be"),         # bf16 out
@@ -179,6 +187,9 @@ def test_bindings_refuse_wrong_dtypes_and_shapes():
         (decode, dict(sl=torch.zeros(B, dtype=torch.int64)), "seq_lens must be"),
         (update, dict(kn=torch.zeros((T, 4, 128), dtype=f32)), "k_new must be"),
         (update, dict(pt=torch.zeros((B, 3), dtype=torch.int16)), "page_table must be"),
+        (append, dict(kn=torch.zeros((B + 1, 4, 128), dtype=bf)), "k_new must have"),    # one row per sequence
+        (append, dict(kn=torch.zeros((B, 4, 128), dtype=f32)), "k_new must be"),
+        (append, dict(out=torch.zeros((B, 64, 128), dtype=bf)), "out must be"),
     ]
     for fn, kw, msg in bad_cases:
         with pytest.raises(bi.BiAttnError, match=msg):
