@@ -2,7 +2,8 @@
 """Benchmark of the batch-invariant paged attention path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input: the page update of
-the step's new tokens, then attention. The headline workload is the bf16 decode sweep at its
+the step's new tokens, then attention (a decode step is `bi_attn_decode_append`, whose split
+kernel also writes the new tokens into their pages, then the combine). The headline workload is the bf16 decode sweep at its
 largest batch (64 sequences, 32 query heads, 4 KV heads, head_dim 128, context lengths
 U[128, 8192], 16-token pages in a shuffled pool, fixed split size 256); ``value`` is its
 algorithmic HBM GB/s. The chunked-prefill workload (16 sequences, 64/4 heads, cached prefix
@@ -15,6 +16,7 @@ against the fp64 oracle (the headline decode rows, sampled prefill and long-cont
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
                        [--no-long] [--no-trace]
+       (profiling: --profile-run, --prefill-only, --long-only, --next-rows-only, --copy-calib-mb)
 """
 
 from __future__ import annotations
@@ -503,6 +505,7 @@ def run_long_decode_bench(args, result):
         "combine_stats": stats_ms([t.ms(1, 2) for t in tms]),
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128,1,append>", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic("decode_split_kernel_long"),
                      "bytes_per_launch": nb["split_kernel"], "avg_launch_ms": float(np.median(part))},
         "invariance": "bitwise: sequences 0 and 5 alone at B=1 equal to the B=8 call",
         "config": {"workload": "long_decode_bf16: 8 sequences x 131072 tokens, Hq 64, Hkv 4, D 128, "
@@ -795,6 +798,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode workload")
     ap.add_argument("--no-trace", action="store_true", help="skip the mixed-trace workload")
+    ap.add_argument("--long-only", action="store_true",
+                    help="measure the long-context decode workload alone (no headline value; for "
+                         "profiling its kernels)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="measure the prefill workload alone (no headline value)")
     ap.add_argument("--cpu-samples", type=int, default=64)
@@ -834,6 +840,10 @@ def main():
     if args.next_rows_only:
         run_rmsnorm_bench(args, result)
         run_gemm_bench(args, result)
+        print(json.dumps(result), flush=True)
+        return
+    if args.long_only:
+        run_long_decode_bench(args, result)
         print(json.dumps(result), flush=True)
         return
     if args.prefill_only:

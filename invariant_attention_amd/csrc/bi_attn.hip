@@ -148,8 +148,9 @@ __global__ __launch_bounds__((64 * DecWaves<E, NB>::value), 1) void decode_split
   // Work items are the pairs I = i Hkv + h of split item i (below) and KV head h. Workgroup k
   // owns I = k, k + G, k + 2G, ... (G workgroups), and its waves take the next of those from a
   // counter in LDS whenever they need one: the two waves that share a SIMD do not progress at
-  // the same rate (issue arbitration favours the older one), so a fixed share per wave would
-  // leave the faster ones idle at the end. Which wave computes a split does not change its bits.
+  // the same rate (with a fixed share per wave, the second wave of each SIMD finished about
+  // 1.35x later than the first), so a fixed share would leave the faster ones idle at the end.
+  // Which wave computes a split does not change its bits.
   __shared__ int lds_next;
   // per wave: one split's accumulators [NB 16 rows][D], staged for contiguous stores (only
   // this wave touches its slice, and one wave's LDS accesses complete in order)
