@@ -77,12 +77,14 @@ __global__ __launch_bounds__(64 * kNormWaves) void rmsnorm_kernel(const char* x,
     const u32x4* xr = (const u32x4*)(x + (size_t)r * chunks * 16);
     u32x4* yr = (u32x4*)(y + (size_t)r * chunks * 16);
     // lane's chunks lane, lane + 64, ...: squares summed in that order
+    // (the chunks held in registers are read and written once: non-temporal loads and stores,
+    // measurably faster; the weight row is shared by every row and stays cached)
     u32x4 xc[kCache], wc[kCache];
 #pragma unroll
     for (int k = 0; k < kCache; ++k) {
       const int ch = lane + 64 * k;
       if (ch < chunks) {
-        xc[k] = xr[ch];
+        xc[k] = __builtin_nontemporal_load(xr + ch);
         wc[k] = ((const u32x4*)w)[ch];
       }
     }
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(64 * kNormWaves) void rmsnorm_kernel(const char* x,
 #pragma unroll
     for (int k = 0; k < kCache; ++k) {
       const int ch = lane + 64 * k;
-      if (ch < chunks) yr[ch] = chunk_out<BF>(xc[k], wc[k], rs);
+      if (ch < chunks) __builtin_nontemporal_store(chunk_out<BF>(xc[k], wc[k], rs), yr + ch);
     }
     for (int ch = lane + 64 * kCache; ch < chunks; ch += 64) yr[ch] = chunk_out<BF>(xr[ch], ((const u32x4*)w)[ch], rs);
   }

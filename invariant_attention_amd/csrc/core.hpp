@@ -128,6 +128,13 @@ template <int D> struct Frag<__bf16, D> {
   __device__ static inline KOp zero_k() { return u32x4{0, 0, 0, 0}; }
   // raw V chunk of lane column c from a V row
   __device__ static inline VRow v_row(const char* row, int c) { return *(const VRow*)(row + NM * c * 2); }
+  // the same loads marked non-temporal (streaming: data read once, not kept in the caches)
+  __device__ static inline KOp k_op_nt(const char* row, int st, int g) {
+    return __builtin_nontemporal_load((const u32x4*)(row + (32 * st + 8 * g) * 2));
+  }
+  __device__ static inline VRow v_row_nt(const char* row, int c) {
+    return __builtin_nontemporal_load((const VRow*)(row + NM * c * 2));
+  }
   // the inverses of k_op and v_row: a lane's part of a K or V row back to memory
   __device__ static inline void store_k(char* row, int st, int g, KOp x) { *(u32x4*)(row + (32 * st + 8 * g) * 2) = x; }
   __device__ static inline void store_v(char* row, int c, VRow x) { *(VRow*)(row + NM * c * 2) = x; }
@@ -295,6 +302,20 @@ template <int D> struct Frag<float, D> {
 #pragma unroll
     for (int s = 0; s < NM / 4; ++s) {
       const f32x4 t = p[s];
+      r.v[4 * s] = t[0]; r.v[4 * s + 1] = t[1]; r.v[4 * s + 2] = t[2]; r.v[4 * s + 3] = t[3];
+    }
+    return r;
+  }
+  // the same loads marked non-temporal (streaming: data read once, not kept in the caches)
+  __device__ static inline KOp k_op_nt(const char* row, int st, int g) {
+    return __builtin_nontemporal_load((const float*)(row + (NKS * g + st) * 4));
+  }
+  __device__ static inline VRow v_row_nt(const char* row, int c) {
+    VRow r;
+    const f32x4* p = (const f32x4*)(row + NM * c * 4);
+#pragma unroll
+    for (int s = 0; s < NM / 4; ++s) {
+      const f32x4 t = __builtin_nontemporal_load(p + s);
       r.v[4 * s] = t[0]; r.v[4 * s + 1] = t[1]; r.v[4 * s + 2] = t[2]; r.v[4 * s + 3] = t[3];
     }
     return r;
