@@ -461,109 +461,137 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
                   vmax3(x[b][0][3], x[b][1][0], vmax3(x[b][1][1], x[b][1][2], x[b][1][3])));
   }
   float mnew[NB], alpha[NB], lnew[NB];
+  // The common sub-tile of a long prefill: not the split's first, no masked key, no row that
+  // needs P_lo, and no lane above its row's gate. The general code then keeps every reference
+  // (alpha = 1, l' = fma(l, 1, rs), no rescale) and the peaked flags; this branch is that code
+  // with those values put in, so it gives the same bits without the decision chain.
+  bool fast = false;
+  if constexpr (PIPE) {
+    if (!first && !mask && !lo_pos_w && lo_wave == 0) {
+      unsigned long long hit = 0;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    mnew[b] = st[b].m;
-    alpha[b] = 1.0f;
-  }
-  bool rescale = false;
-  // Past the split's first sub-tile, a sub-tile none of whose lanes holds a raw score above
-  // its row's gate needs no decision: the gate is at least one base-2 unit below m + kLazy
-  // once scaled (m is at least the first sub-tile's max, so at least its mean), so no row
-  // raises its reference, and the peaked flag stays as it is. One compare per block.
-  unsigned long long gate_hit = 0;
-  if (!first) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) gate_hit |= __builtin_amdgcn_ballot_w64(mxl[b] > st[b].gate);
-  }
-  if (first || gate_hit != 0) {
-    // A row raises its reference only if some lane of it holds a scaled score above
-    // m + kLazy (the scaled row max is the max of the lanes' scaled maxima: rounding is
-    // monotonic), so the row max butterfly runs only at a split start or when some lane of the
-    // wave needs it.
-    bool full = first;
-    if (!first) {
-      unsigned long long up = 0;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) up |= __builtin_amdgcn_ballot_w64(mxl[b] * cscale > st[b].m + kLazy);
-      full = up != 0;
+      for (int b = 0; b < NB; ++b) hit |= __builtin_amdgcn_ballot_w64(mxl[b] > st[b].gate);
+      fast = hit == 0;
     }
-    if (full) {
-      unsigned long long need_any = 0;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float rm = xor_max(mxl[b]);
-        const float mt = rm * cscale;
-        if (first) {
-          // an all-masked row (a prefill row below the split's first key) takes the reference
-          // -FLT_MAX, so its p = 2^-inf = 0 with a finite offset
-          mnew[b] = mt > -3.40282347e38f ? mt : -3.40282347e38f;
-          // gate of the peaked-split test: (mean of the row's unmasked scaled scores + kGap) /
-          // cscale: the lane's scores summed in a fixed order, the row sum by the xor butterfly
-          // (every lane of the row gets the same bits), divided by the unmasked count
-          // min(32, pos - key0 + 1) through v_rcp_f32; an all-masked row gets 0 * inf = NaN,
-          // which never tests true
-          float sum = 0.f, rcnt = 1.0f / kSubTile;
-          if (mask) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) sum = sum + (x[b][kb][r] > -__builtin_inff() ? x[b][kb][r] : 0.f);
-            rcnt = __builtin_amdgcn_rcpf((float)min(max(pos[b] - key0 + 1, 0), kSubTile));
-          } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) sum = sum + x[b][kb][r];
-          }
-          sum = xor_sum(sum);
-          st[b].gate = (sum * cscale * rcnt + kGap) * __builtin_amdgcn_rcpf(cscale);
-          st[b].lo = false;
-        } else {
-          const bool need = mt > st[b].m + kLazy;
-          if (need) {
-            mnew[b] = mt;
-            alpha[b] = ex2(st[b].m - mt);
-          }
-          need_any |= __builtin_amdgcn_ballot_w64(need);
-        }
-      }
-      rescale = !first && need_any != 0;
-    }
-    // the split's peaked flag (per row, sticky): a ballot of the lanes above their row's gate,
-    // read out for the lanes c, c + 16, c + 32, c + 48 of each row
-    const int col = (int)(threadIdx.x & 15);
-    unsigned long long any_lo = 0;
+  }
+  if (fast) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const unsigned long long up = __builtin_amdgcn_ballot_w64(mxl[b] > st[b].gate);
-      st[b].lo = st[b].lo || ((up >> col) & 0x0001000100010001ull) != 0;
-      any_lo |= __builtin_amdgcn_ballot_w64(st[b].lo);
+      mnew[b] = st[b].m;
+      const float nm = -st[b].m;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[b][kb][r], cscale, nm));
+      const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
+                       ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
+      lnew[b] = __builtin_fmaf(st[b].l, 1.0f, rs);
     }
-    lo_wave = any_lo != 0;
-  }
+  } else {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const float nm = -mnew[b];
+    for (int b = 0; b < NB; ++b) {
+      mnew[b] = st[b].m;
+      alpha[b] = 1.0f;
+    }
+    bool rescale = false;
+    // Past the split's first sub-tile, a sub-tile none of whose lanes holds a raw score above
+    // its row's gate needs no decision: the gate is at least one base-2 unit below m + kLazy
+    // once scaled (m is at least the first sub-tile's max, so at least its mean), so no row
+    // raises its reference, and the peaked flag stays as it is. One compare per block.
+    unsigned long long gate_hit = 0;
+    if (!first) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int b = 0; b < NB; ++b) gate_hit |= __builtin_amdgcn_ballot_w64(mxl[b] > st[b].gate);
+    }
+    if (first || gate_hit != 0) {
+      // A row raises its reference only if some lane of it holds a scaled score above
+      // m + kLazy (the scaled row max is the max of the lanes' scaled maxima: rounding is
+      // monotonic), so the row max butterfly runs only at a split start or when some lane of the
+      // wave needs it.
+      bool full = first;
+      if (!first) {
+        unsigned long long up = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[b][kb][r], cscale, nm));
-    const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
-                     ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
-    lnew[b] = first ? rs : __builtin_fmaf(st[b].l, alpha[b], rs);
-  }
-  if (first) {
+        for (int b = 0; b < NB; ++b) up |= __builtin_amdgcn_ballot_w64(mxl[b] * cscale > st[b].m + kLazy);
+        full = up != 0;
+      }
+      if (full) {
+        unsigned long long need_any = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+          const float rm = xor_max(mxl[b]);
+          const float mt = rm * cscale;
+          if (first) {
+            // an all-masked row (a prefill row below the split's first key) takes the reference
+            // -FLT_MAX, so its p = 2^-inf = 0 with a finite offset
+            mnew[b] = mt > -3.40282347e38f ? mt : -3.40282347e38f;
+            // gate of the peaked-split test: (mean of the row's unmasked scaled scores + kGap) /
+            // cscale: the lane's scores summed in a fixed order, the row sum by the xor butterfly
+            // (every lane of the row gets the same bits), divided by the unmasked count
+            // min(32, pos - key0 + 1) through v_rcp_f32; an all-masked row gets 0 * inf = NaN,
+            // which never tests true
+            float sum = 0.f, rcnt = 1.0f / kSubTile;
+            if (mask) {
 #pragma unroll
-      for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else if (rescale) {
-    // alpha == 1 exactly for rows that kept their reference, so x * alpha == x
+              for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+                for (int r = 0; r < 4; ++r) sum = sum + (x[b][kb][r] > -__builtin_inff() ? x[b][kb][r] : 0.f);
+              rcnt = __builtin_amdgcn_rcpf((float)min(max(pos[b] - key0 + 1, 0), kSubTile));
+            } else {
 #pragma unroll
-      for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sum = sum + x[b][kb][r];
+            }
+            sum = xor_sum(sum);
+            st[b].gate = (sum * cscale * rcnt + kGap) * __builtin_amdgcn_rcpf(cscale);
+            st[b].lo = false;
+          } else {
+            const bool need = mt > st[b].m + kLazy;
+            if (need) {
+              mnew[b] = mt;
+              alpha[b] = ex2(st[b].m - mt);
+            }
+            need_any |= __builtin_amdgcn_ballot_w64(need);
+          }
+        }
+        rescale = !first && need_any != 0;
+      }
+      // the split's peaked flag (per row, sticky): a ballot of the lanes above their row's gate,
+      // read out for the lanes c, c + 16, c + 32, c + 48 of each row
+      const int col = (int)(threadIdx.x & 15);
+      unsigned long long any_lo = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const unsigned long long up = __builtin_amdgcn_ballot_w64(mxl[b] > st[b].gate);
+        st[b].lo = st[b].lo || ((up >> col) & 0x0001000100010001ull) != 0;
+        any_lo |= __builtin_amdgcn_ballot_w64(st[b].lo);
+      }
+      lo_wave = any_lo != 0;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float nm = -mnew[b];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[b][kb][r], cscale, nm));
+      const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
+                       ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
+      lnew[b] = first ? rs : __builtin_fmaf(st[b].l, alpha[b], rs);
+    }
+    if (first) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if (rescale) {
+      // alpha == 1 exactly for rows that kept their reference, so x * alpha == x
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mb = 0; mb < NM; ++mb) st[b].acc[mb] = st[b].acc[mb] * alpha[b];
+    }
   }
   // P_lo choice of this lane's keys: the row's position or the split's peaked flag
   bool lo_row[NB];
