@@ -959,14 +959,29 @@ __global__ __launch_bounds__(64 * NW, MINB) void prefill_kernel(AttnParams a) {
       for (int cb = 0; cb < NBW; ++cb) {
         if (blk_max[cb] < j * S) continue;
         float fa, fb;
+        // the product A a of fold_elem() is A itself in every lane that keeps its reference
+        // (a = 1), so it is formed only when some lane of the wave raises (rarely past split 0)
+        const bool scale = wave_any(fold_raises(Mrow[cb], st[cb].m));
         fold_scalars(Mrow[cb], Lrow[cb], st[cb].m, row_l(st[cb]), fa, fb);
+        if (AREG) {
+          if (scale) {
 #pragma unroll
-        for (int mb = 0; mb < NM; ++mb) {
-          f32x4& slot = AREG ? Areg[AREG ? cb : 0][mb] : lds_A[AREG ? 0 : wave][AREG ? 0 : cb][AREG ? 0 : mb][lane];
-          f32x4 A = (AREG || j > 0) ? slot : f32x4{0.f, 0.f, 0.f, 0.f};   // (LDS slots start unwritten)
+            for (int mb = 0; mb < NM; ++mb) Areg[AREG ? cb : 0][mb] = Areg[AREG ? cb : 0][mb] * fa;
+          }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb);
-          slot = A;
+          for (int mb = 0; mb < NM; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              Areg[AREG ? cb : 0][mb][e] = __builtin_fmaf(st[cb].acc[mb][e], fb, Areg[AREG ? cb : 0][mb][e]);
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < NM; ++mb) {
+            f32x4& slot = lds_A[AREG ? 0 : wave][AREG ? 0 : cb][AREG ? 0 : mb][lane];
+            f32x4 A = j > 0 ? slot : f32x4{0.f, 0.f, 0.f, 0.f};   // (LDS slots start unwritten)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) A[e] = fold_elem(A[e], st[cb].acc[mb][e], fa, fb);
+            slot = A;
+          }
         }
       }
     }

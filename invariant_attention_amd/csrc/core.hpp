@@ -99,6 +99,18 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned bf16_pack2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+// c plus the eight bf16 values of a lane's P words, one word (two values) at a time in word
+// order, each with one v_dot2c_f32_bf16 against (1, 1): the products are exact and the pair's
+// sum is added to c in fp32. Words of zeros leave c as it is.
+// (The words are copied out of the vector by name before the bit_cast: a bit_cast of an
+// indexed element of an ext_vector_type vector compiles to a read of element 0 here.)
+__device__ __forceinline__ float add_words(float c, u32x4 w) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const unsigned e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, e[k]), one, c, false);
+  return c;
+}
 __device__ __forceinline__ float bf16_lo_f(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi_f(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
@@ -194,9 +206,12 @@ template <int D> struct Frag<__bf16, D> {
       vf1 = vn;
     }
   }
+  // l: on entry the row state's part carried into this sub-tile (0 at a split start), on return
+  // with the lane's P_hi words added and then its P_lo words (zero words where P_lo is not
+  // used), so that l sums exactly the weights the accumulator received.
   template <int NB, bool PIPE = false, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4],
-                                   const bool (&lo_row)[NB], bool lo_any) {
+                                   float (&l)[NB], const bool (&lo_row)[NB], bool lo_any) {
     u32x4 H[NB], L[NB];
     auto make_lo = [&](int b) {
       unsigned lo[4];
@@ -214,14 +229,21 @@ template <int D> struct Frag<__bf16, D> {
 #pragma unroll
       for (int i = 0; i < 4; ++i) hi[i] = bf16_pack2(p[b][i >> 1][(2 * i) & 3], p[b][i >> 1][(2 * i + 1) & 3]);
       H[b] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      if (!PIPE) make_lo(b);
+      l[b] = add_words(l[b], H[b]);
+      if (!PIPE) {
+        make_lo(b);
+        l[b] = add_words(l[b], L[b]);
+      }
     }
     if constexpr (PIPE) {
       // LDS operands: the hi pass, then (only when some row needs it) the lo pass
       pv_pass<NB, PIPE>(acc, getV, H);
       if (lo_any) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) make_lo(b);
+        for (int b = 0; b < NB; ++b) {
+          make_lo(b);
+          l[b] = add_words(l[b], L[b]);
+        }
         asm volatile("" ::: "memory");   // the V operands are read again, not kept
         pv_pass<NB, PIPE>(acc, getV, L);
       }
@@ -361,7 +383,7 @@ template <int D> struct Frag<float, D> {
   // getV(i) returns the lane's raw V chunk (NM floats, dims NM c .. NM c + NM) of key slot i.
   template <int NB, bool PIPE = false, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4],
-                                   const bool (&)[NB], bool) {
+                                   float (&)[NB], const bool (&)[NB], bool) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const VRow row = getV(i);
@@ -380,7 +402,8 @@ template <int D> struct Frag<float, D> {
 // by more than kLazy (so p <= 2^kLazy). The result is the same softmax; skipping most
 // rescales removes the acc *= alpha multiplies from most sub-tiles. The decision depends on
 // the row's own numbers only, so every route makes the same one.
-// l is kept per lane (the sum of the p values the lane holds); the row's l is the sum of its
+// l is kept per lane: the sum of the weights the lane's PV products used (bf16 data: its P_hi
+// and P_lo values, added by Frag::pv; fp32 data: its p values); the row's l is the sum of its
 // four lanes' partials, taken once per split by row_l().
 constexpr float kLazy = 8.0f;
 // Precision of P in the bf16 PV product. P_hi = bf16(p) alone carries a relative error up to
@@ -461,9 +484,10 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
                   vmax3(x[b][0][3], x[b][1][0], vmax3(x[b][1][1], x[b][1][2], x[b][1][3])));
   }
   float mnew[NB], alpha[NB], lnew[NB];
+  constexpr bool BF = std::is_same<E, __bf16>::value;
   // The common sub-tile of a long prefill: not the split's first, no masked key, no row that
   // needs P_lo, and no lane above its row's gate. The general code then keeps every reference
-  // (alpha = 1, l' = fma(l, 1, rs), no rescale) and the peaked flags; this branch is that code
+  // (alpha = 1, l carried as it is, no rescale) and the peaked flags; this branch is that code
   // with those values put in, so it gives the same bits without the decision chain.
   bool fast = false;
   if constexpr (PIPE) {
@@ -483,9 +507,13 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[b][kb][r], cscale, nm));
-      const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
-                       ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
-      lnew[b] = __builtin_fmaf(st[b].l, 1.0f, rs);
+      if constexpr (BF) {
+        lnew[b] = st[b].l;   // the P words are added by pv()
+      } else {
+        const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
+                         ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
+        lnew[b] = __builtin_fmaf(st[b].l, 1.0f, rs);
+      }
     }
   } else {
 #pragma unroll
@@ -576,9 +604,15 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[b][kb][r] = ex2(__builtin_fmaf(x[b][kb][r], cscale, nm));
-      const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
-                       ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
-      lnew[b] = first ? rs : __builtin_fmaf(st[b].l, alpha[b], rs);
+      if constexpr (BF) {
+        // the part of l carried into the sub-tile (l alpha is l itself where the reference
+        // stays); pv() adds the P words
+        lnew[b] = first ? 0.f : st[b].l * alpha[b];
+      } else {
+        const float rs = ((p[b][0][0] + p[b][0][1]) + (p[b][0][2] + p[b][0][3])) +
+                         ((p[b][1][0] + p[b][1][1]) + (p[b][1][2] + p[b][1][3]));
+        lnew[b] = first ? rs : __builtin_fmaf(st[b].l, alpha[b], rs);
+      }
     }
     if (first) {
 #pragma unroll
@@ -603,7 +637,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int mb = 0; mb < NM; ++mb) accl[b][mb] = st[b].acc[mb];
-  F::template pv<NB, PIPE>(accl, getV, p, lo_row, lo_any);
+  F::template pv<NB, PIPE>(accl, getV, p, lnew, lo_row, lo_any);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     st[b].m = mnew[b];
@@ -614,18 +648,24 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
 }
 
 // Ascending fold of split j's state into the row state (the same function the combine kernel
-// applies element by element): M' = max(M, m), a = 2^(M - M'), b = 2^(m - M'),
-// L = l b + L a, A = acc b + A a, each one fma with the rounded product of the row state as
-// addend (so A can be updated in place). The row state starts at (M, L, A) = (-inf, 0, 0), so
-// split 0 gives a = 0, b = 1 and copies its state exactly (x 1 + 0 = x for the never
-// negative-zero partials) with no special case; an empty split (m = -FLT_MAX, l = 0,
-// acc = 0) gives a = 1, b = 0 and leaves a row state with finite M as it was.
+// applies element by element), with a lazy row reference like the one inside a split: M is
+// raised to the split's m only when m exceeds it by more than kLazy, and then a = 2^(M - m),
+// b = 1; otherwise M stays, a = 1 and b = 2^(m - M) <= 2^kLazy. L = l b + L a and
+// A = acc b + A a, each one fma with the rounded product of the row state as addend (so A can
+// be updated in place). Where a = 1 that product is the row state itself, so a caller may skip
+// the multiply when no lane raises (fold_raises) and still get the same bits. The row state
+// starts at (M, L, A) = (-inf, 0, 0), so split 0 raises (a = 0, b = 1) and copies its state
+// exactly (x 1 + 0 = x for the never negative-zero partials) with no special case; an empty
+// split (m = -FLT_MAX, l = 0, acc = 0) after a finite M gives b = 0 and leaves the row state as
+// it was; a NaN m or M gives b = NaN, so the row comes out NaN.
+__device__ __forceinline__ bool fold_raises(float M, float m) { return m > M + kLazy; }
 __device__ __forceinline__ void fold_scalars(float& M, float& L, float m, float l, float& a, float& b) {
-  const float Mn = fmaxf(M, m);
-  a = ex2(M - Mn);
-  b = ex2(m - Mn);
+  const bool up = fold_raises(M, m);
+  const float e = ex2(up ? M - m : m - M);
+  a = up ? e : 1.0f;
+  b = up ? 1.0f : e;
   L = __builtin_fmaf(l, b, L * a);
-  M = Mn;
+  M = up ? m : M;
 }
 __device__ __forceinline__ float fold_elem(float A, float acc, float a, float b) {
   return __builtin_fmaf(acc, b, A * a);

@@ -11,11 +11,14 @@ term of P) can be studied over whole workloads on the CPU:
   at ``-inf``; lane ``g`` of a row holds keys ``16 kb + 4 g + r`` (kb < 2, r < 4);
 * a lazy reference maximum: set from the split's first sub-tile, raised (with
   ``acc *= 2^(m - m')``) only when a sub-tile's row max exceeds it by more than 8;
-* ``p = 2^(fma(x, c, -m))``, lane sums of p in a fixed order, ``P_hi = bf16(p)`` and, where
-  the rule asks for it, ``P_lo = bf16(p - P_hi)``, both multiplied into V with fp32
-  accumulation (hi first, then lo);
-* the split partials folded in ascending order:
-  ``M' = max(M, m), a = 2^(M - M'), b = 2^(m - M'), L = fma(l, b, L a), A = fma(acc, b, A a)``.
+* ``p = 2^(fma(x, c, -m))``, ``P_hi = bf16(p)`` and, where the rule asks for it,
+  ``P_lo = bf16(p - P_hi)``, both multiplied into V with fp32 accumulation (hi first, then lo);
+  the lane's l is the carried part (0 at a split start, else ``l alpha``) plus its P_hi values
+  two at a time in a fixed order, then its P_lo values the same way, so l sums exactly the
+  weights the accumulator received;
+* the split partials folded in ascending order with a lazy row reference: M is raised to the
+  split's m (``a = 2^(M - m), b = 1``) only when m exceeds it by more than 8, else
+  ``a = 1, b = 2^(m - M)``; ``L = fma(l, b, L a), A = fma(acc, b, A a)``.
 
 Rules for the second bf16 term (``rule``):
   ``"kernel"``   the rule the kernels apply: rows at positions below 1024, and every key
@@ -117,10 +120,7 @@ def attend_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray,
                 alpha = np.where(need, np.exp2(np.where(need, m - mt, 0).astype(F32)), F32(1)).astype(F32)
             p = np.exp2(_fma(x, c, -mnew[:, :, None, None, None])).astype(F32)
             p = np.where(np.isnan(p), F32(0), p).astype(F32)
-            # lane sum: ((p00 + p01) + (p02 + p03)) + ((p10 + p11) + (p12 + p13))
-            p_l = p.transpose(0, 1, 3, 2, 4)                     # [R][J][g][kb][r]
-            rs = (_pair_sum(p_l[:, :, :, 0]) + _pair_sum(p_l[:, :, :, 1])).astype(F32)
-            l_lane = rs if t == 0 else _fma(l_lane, alpha[:, :, None], rs)
+            l_lane = np.zeros_like(l_lane) if t == 0 else (l_lane * alpha[:, :, None]).astype(F32)
             acc = np.zeros_like(acc) if t == 0 else (acc * alpha[:, :, None]).astype(F32)
             # sticky peaked flag: some lane of the row above the threshold
             lo_split = lo_split | ((lane_max * c).astype(F32) > thr[:, :, None]).any(axis=2)
@@ -140,6 +140,14 @@ def attend_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray,
                 stats["lo_lanes"] = stats.get("lo_lanes", 0) + int((live & lo_lane).sum())
             ph = bf16_round(p)
             pl = np.where(lo_lane[:, :, None, :, None], bf16_round((p - ph).astype(F32)), F32(0)).astype(F32)
+            # the lane's l: its P_hi values, then its P_lo values, two at a time in the order
+            # (kb 0, r 0-1), (kb 0, r 2-3), (kb 1, r 0-1), (kb 1, r 2-3)
+            for w in (ph, pl):
+                wl = w.transpose(0, 1, 3, 2, 4)                  # [R][J][g][kb][r]
+                for kb in range(2):
+                    for r in (0, 2):
+                        pair = (wl[:, :, :, kb, r] + wl[:, :, :, kb, r + 1]).astype(F32)
+                        l_lane = (l_lane + pair).astype(F32)
             # back to key order 16 kb + 4 g + r
             ph_k = ph.reshape(R, J, 32)
             pl_k = pl.reshape(R, J, 32)
@@ -158,12 +166,13 @@ def attend_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray,
             mj = np.where(ok, m[:, j], NEG_MAX).astype(F32)
             lj = np.where(ok, l_row[:, j], F32(0)).astype(F32)
             aj = np.where(ok[:, None], acc[:, j], F32(0)).astype(F32)
-            Mn = np.maximum(M, mj).astype(F32)
-            a = np.exp2((M - Mn).astype(F32)).astype(F32)
-            b = np.exp2((mj - Mn).astype(F32)).astype(F32)
+            up = mj > (M + LAZY).astype(F32)
+            e = np.exp2(np.where(up, M - mj, mj - M).astype(F32)).astype(F32)
+            a = np.where(up, e, F32(1)).astype(F32)
+            b = np.where(up, F32(1), e).astype(F32)
             Lr = _fma(lj, b, (Lr * a).astype(F32))
             A = _fma(aj, b[:, None], (A * a[:, None]).astype(F32))
-            M = Mn
+            M = np.where(up, mj, M).astype(F32)
     return (A / Lr[:, None]).astype(F32)
 
 
