@@ -161,11 +161,50 @@ template <int D> struct Frag<__bf16, D> {
   }
   // Each score block s[b][kb] accumulates its k-steps in ascending order; the 2 NB chains are
   // interleaved k-step by k-step so that consecutive MFMAs are independent. PIPE (operands
-  // read from LDS): the reads of k-step st + 1 are issued before the MFMAs of k-step st.
+  // read from LDS): k-step 0 is read and waited for alone, then the reads of k-steps
+  // [1, C) go out before the MFMAs of k-step 0 and those of [C, NKS) before the MFMAs of
+  // [1, C) (C = 1 + NKS / 2), each batch after the previous one has landed, as in pv_pass.
+  // Otherwise the reads of k-step st + 1 are issued before the MFMAs of k-step st.
   template <int NB, bool PIPE = false, class KGet>
   __device__ static inline void qk(f32x4 (&s)[NB][2], KGet& getK, const Q (&q)[NB]) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) s[b][0] = s[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (PIPE) {
+      constexpr int C = 1 + NKS / 2;
+      constexpr int kWaitLgkm0 = 0xC07F;   // s_waitcnt lgkmcnt(0) alone
+      u32x4 k[NKS][2];
+      auto mfmas = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          s[b][0] = mma_bf16(k[st][0], q[b].v[st], s[b][0]);
+          s[b][1] = mma_bf16(k[st][1], q[b].v[st], s[b][1]);
+        }
+      };
+      k[0][0] = getK(0, 0);
+      k[0][1] = getK(1, 0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+      for (int st = 1; st < C; ++st) {
+        k[st][0] = getK(0, st);
+        k[st][1] = getK(1, st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+      for (int st = C; st < NKS; ++st) {
+        k[st][0] = getK(0, st);
+        k[st][1] = getK(1, st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 1; st < C; ++st) mfmas(st);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = C; st < NKS; ++st) mfmas(st);
+      return;
+    }
     u32x4 k0 = getK(0, 0), k1 = getK(1, 0);
 #pragma unroll
     for (int st = 0; st < NKS; ++st) {
@@ -192,26 +231,62 @@ template <int D> struct Frag<__bf16, D> {
   // getV(mb) returns the A operand of row block mb: 8 bf16 of one head-dim row d for the key
   // slots vkey(0..7, g). Which d a (row block, lane) holds is the caller's choice; each
   // output element's dot product is the same whichever MFMA row computes it.
+  // PIPE (LDS operands): the operands of the first NPRE row blocks (vpre) were read by the caller
+  // ahead of time; the other row blocks' reads go out in two batches, each issued right after
+  // the previous batch has landed and before the MFMAs of that batch, which run while it lands.
+  // (The compiler drains every outstanding LDS read at each wait here, so the waits are placed
+  // explicitly where nothing newer is in flight.) Otherwise the reads of row block mb + 2 are
+  // issued before the MFMAs of row block mb.
+  static constexpr int NPRE = 2;
   template <int NB, bool PIPE, class VGet>
-  __device__ static inline void pv_pass(f32x4 (&acc)[NB][NM], VGet& getV, const u32x4 (&P)[NB]) {
-    u32x4 vf = getV(0), vf1 = getV(1);
+  __device__ static inline void pv_pass(f32x4 (&acc)[NB][NM], VGet& getV, const u32x4 (&P)[NB],
+                                        const u32x4 (&vpre)[NPRE]) {
+    if constexpr (PIPE) {
+      constexpr int B1 = NPRE, B2 = NPRE + (NM - NPRE + 1) / 2;   // batches [0,B1) [B1,B2) [B2,NM)
+      constexpr int kWaitLgkm0 = 0xC07F;                          // s_waitcnt lgkmcnt(0) alone
+      u32x4 v[NM];
 #pragma unroll
-    for (int mb = 0; mb < NM; ++mb) {
-      // PIPE: the reads of row block mb + 2 are issued before the MFMAs of row block mb
-      const u32x4 vn = mb + 2 < NM ? getV(mb + 2) : vf;
-      if (PIPE) __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < B1; ++i) v[i] = vpre[i];
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b][mb] = mma_bf16(vf, P[b], acc[b][mb]);
-      vf = vf1;
-      vf1 = vn;
+      for (int i = B1; i < B2; ++i) v[i] = getV(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mb = 0; mb < B1; ++mb)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][mb] = mma_bf16(v[mb], P[b], acc[b][mb]);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+      for (int i = B2; i < NM; ++i) v[i] = getV(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mb = B1; mb < B2; ++mb)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][mb] = mma_bf16(v[mb], P[b], acc[b][mb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mb = B2; mb < NM; ++mb)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][mb] = mma_bf16(v[mb], P[b], acc[b][mb]);
+    } else {
+      u32x4 vf = getV(0), vf1 = getV(1);
+#pragma unroll
+      for (int mb = 0; mb < NM; ++mb) {
+        const u32x4 vn = mb + 2 < NM ? getV(mb + 2) : vf;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][mb] = mma_bf16(vf, P[b], acc[b][mb]);
+        vf = vf1;
+        vf1 = vn;
+      }
     }
   }
-  // l: on entry the row state's part carried into this sub-tile (0 at a split start), on return
-  // with the lane's P_hi words added and then its P_lo words (zero words where P_lo is not
-  // used), so that l sums exactly the weights the accumulator received.
+  // PIPE: vpre holds the operands of the first NPRE row blocks, read before the softmax so that
+  // the first PV MFMAs need not wait for LDS.
   template <int NB, bool PIPE = false, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4],
-                                   float (&l)[NB], const bool (&lo_row)[NB], bool lo_any) {
+                                   float (&l)[NB], const bool (&lo_row)[NB], bool lo_any,
+                                   const u32x4 (&vpre)[NPRE]) {
     u32x4 H[NB], L[NB];
     auto make_lo = [&](int b) {
       unsigned lo[4];
@@ -237,7 +312,7 @@ template <int D> struct Frag<__bf16, D> {
     }
     if constexpr (PIPE) {
       // LDS operands: the hi pass, then (only when some row needs it) the lo pass
-      pv_pass<NB, PIPE>(acc, getV, H);
+      pv_pass<NB, PIPE>(acc, getV, H, vpre);
       if (lo_any) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -245,7 +320,10 @@ template <int D> struct Frag<__bf16, D> {
           l[b] = add_words(l[b], L[b]);
         }
         asm volatile("" ::: "memory");   // the V operands are read again, not kept
-        pv_pass<NB, PIPE>(acc, getV, L);
+        u32x4 vre[NPRE];
+#pragma unroll
+        for (int i = 0; i < NPRE; ++i) vre[i] = getV(i);
+        pv_pass<NB, PIPE>(acc, getV, L, vre);
       }
     } else {
       // register operands (an HBM-bound caller): hi and lo MFMA per row block, P_lo zero in
@@ -383,7 +461,7 @@ template <int D> struct Frag<float, D> {
   // getV(i) returns the lane's raw V chunk (NM floats, dims NM c .. NM c + NM) of key slot i.
   template <int NB, bool PIPE = false, class VGet>
   __device__ static inline void pv(f32x4 (&acc)[NB][NM], VGet& getV, const float (&p)[NB][2][4],
-                                   float (&)[NB], const bool (&)[NB], bool) {
+                                   float (&)[NB], const bool (&)[NB], bool, const u32x4 (&)[2]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const VRow row = getV(i);
@@ -464,6 +542,16 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
   for (int b = 0; b < NB; ++b) qv[b] = q[b];
   f32x4 s[NB][2];
   F::template qk<NB, PIPE>(s, getK, qv);
+  // the first PV operands (bf16 with LDS operands), read while the softmax runs
+  constexpr int NPRE = 2;
+  u32x4 vpre[NPRE];
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) vpre[i] = u32x4{0, 0, 0, 0};
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) vpre[i] = getV(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float p[NB][2][4];
   float x[NB][2][4], mxl[NB];
 #pragma unroll
@@ -637,7 +725,7 @@ __device__ __forceinline__ void subtile_step(RowState<D>* st, const typename Fra
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int mb = 0; mb < NM; ++mb) accl[b][mb] = st[b].acc[mb];
-  F::template pv<NB, PIPE>(accl, getV, p, lnew, lo_row, lo_any);
+  F::template pv<NB, PIPE>(accl, getV, p, lnew, lo_row, lo_any, vpre);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     st[b].m = mnew[b];
