@@ -613,6 +613,118 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
   *(V*)o = r;
 }
 
+// Combine for long rows (more than 32 splits). The fold of a row is one sequential chain per
+// element, and with one wave doing both a row's (m, l) fold and its elements' folds, every split
+// cost the whole instruction stream of both. Here a workgroup owns one (sequence, q head) row and
+// splits the chains among its waves, which run side by side: wave 0 runs the row's lazy reference
+// M (fold_raises) and then forms a window's coefficients a, b lane-parallel with fold_scalars
+// itself (lane u: split 64 w + u, from its m and the reference before it), so they carry the bits
+// of the one-wave fold; it hands them over through LDS, one 64-split window at a time (two
+// buffers, one barrier per window). Wave 1 runs L = fma(l, b, L a) as fold_scalars does, and wave
+// 2 + e folds floats [64 e, 64 e + 64) of the row with fold_elem, its accumulator loads 64 splits
+// ahead in a register ring. The output is A / L.
+template <int D>
+__global__ __launch_bounds__(64 * (D / 64 + 2)) void combine_rows_kernel(AttnParams a) {
+  __shared__ float4 coef[2][64];   // [buffer][split of the window] (a, b, l, -)
+  __shared__ float lrow;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int G = a.group;
+  const int row = (int)blockIdx.x;                          // b Hq + h
+  if (row >= a.batch * a.hq) return;                        // (the whole workgroup)
+  const int rg = row / G, hl = row - rg * G, b = rg / a.hkv;
+  const size_t blk0 = (size_t)rg * a.jmax * G;              // split 0 of the row group
+  float* o = a.out + (size_t)row * D;
+  const int seq_len = a.seq_lens[b];
+  if (seq_len <= 0 || seq_len > a.max_seq_len) {
+    if (wave > 1) o[64 * (wave - 2) + lane] = __builtin_nanf("");
+    return;
+  }
+  const int J = (seq_len - 1) / split_len(a, seq_len) + 1;
+  const int nw = (J + 63) / 64;
+  if (wave == 0) {
+    const float2* ml = a.ws_ml + blk0 + hl;                // split j at ml[j G]
+    float M = -__builtin_inff();
+    float2 mw = ml[(size_t)min(lane, J - 1) * G];
+    for (int w = 0; w < nw; ++w) {
+      const float2 mn = ml[(size_t)min(64 * (w + 1) + lane, J - 1) * G];
+      const int cnt = min(64, J - 64 * w);
+      float mprev = M;                                      // lane u: the reference before split 64 w + u
+      auto chain = [&](auto full) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+          if (decltype(full)::value || u < cnt) {
+            const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mw.x), u));
+            mprev = lane == u ? M : mprev;
+            M = fold_raises(M, m) ? m : M;
+          }
+        }
+      };
+      if (cnt == 64) chain(std::true_type{});
+      else chain(std::false_type{});
+      // this lane's split's coefficients, from the same inputs as the chain's
+      float Mu = mprev, Lu = 0.f, fa, fb;
+      fold_scalars(Mu, Lu, mw.x, mw.y, fa, fb);
+      coef[w & 1][lane] = make_float4(fa, fb, mw.y, 0.f);
+      __syncthreads();
+      mw = mn;
+    }
+    __syncthreads();
+  } else if (wave == 1) {
+    float L = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      __syncthreads();                                      // window w's coefficients are in coef[w & 1]
+      const float4 c = coef[w & 1][lane];
+      const int cnt = min(64, J - 64 * w);
+#pragma unroll
+      for (int u = 0; u < 64; ++u) {
+        if (u < cnt) {
+          const float fa = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.x), u));
+          const float fb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.y), u));
+          const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.z), u));
+          L = __builtin_fmaf(l, fb, L * fa);
+        }
+      }
+    }
+    if (lane == 0) lrow = L;
+    __syncthreads();
+  } else {
+    const int e = wave - 2;
+    // split j of this lane's float at byte j S + 4 lane of the wave's base (S = G D 4 bytes);
+    // offsets fit 32 bits (the launcher checks jmax S)
+    const char* base = (const char*)(a.ws_acc + (blk0 + hl) * D + 64 * e);
+    const unsigned S = (unsigned)(G * D * 4), last = (unsigned)(J - 1) * S, lo = 4u * (unsigned)lane;
+    auto ld = [&](unsigned off) { return *(const float*)(base + (off + lo)); };
+    float ring[64];
+    unsigned off = 0;
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      ring[u] = ld(min(off, last));
+      off += S;
+    }
+    float A = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      __syncthreads();                                      // window w's coefficients are in coef[w & 1]
+      const int cnt = min(64, J - 64 * w);
+      auto fold = [&](auto full) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+          if (decltype(full)::value || u < cnt) {
+            const float2 c = *(const float2*)&coef[w & 1][u];   // (a, b), the same in every lane
+            A = fold_elem(A, ring[u], c.x, c.y);
+          }
+          ring[u] = ld(min(off, last));
+          off += S;
+        }
+      };
+      if (cnt == 64) fold(std::true_type{});
+      else fold(std::false_type{});
+    }
+    __syncthreads();                                        // wave 1's L is in lrow
+    o[64 * e + lane] = A / lrow;
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Prefill: a workgroup owns a tile of query columns (token-major: column = token * G + head)
 // of one (sequence, KV head) and walks every 32-key sub-tile that any of its rows needs, in
@@ -1343,6 +1455,8 @@ void launch_combine_w(const AttnParams& a, hipStream_t s) {
 template <int D>
 void launch_combine_d(const AttnParams& a, hipStream_t s) {
   if (a.jmax <= 32) launch_combine_w<D, 4, 32>(a, s);
+  else if ((int64_t)a.jmax * a.group * D * 4 < ((int64_t)1 << 31))
+    hipLaunchKernelGGL((combine_rows_kernel<D>), dim3((unsigned)(a.batch * a.hq)), dim3(64 * (D / 64 + 2)), 0, s, a);
   else launch_combine_w<D, 1, 64>(a, s);
 }
 int launch_combine(const AttnParams& a, int D, hipStream_t s) {

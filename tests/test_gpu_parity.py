@@ -108,6 +108,36 @@ def test_split_edges_single_sequence():
         assert_bitwise(outp, torch.from_numpy(out), f"decode vs prefill L={L}")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
+def test_long_rows_combine_windows(d, dtype):
+    """Decode with rows of 1 to 200 splits in one call (the combine for rows of more than 32
+    splits hands coefficients over in 64-split windows): windows that end exactly, one split
+    past a window, a single split; every row bitwise equal to the prefill of the same token,
+    sampled rows against the oracle, and rows of invalid length NaN without touching the rest."""
+    shape = AttnShape(8, 2, d, 16, 256, dtype)
+    cfg = cfg_for(shape)
+    lens = [100, 256 * 63, 256 * 64, 256 * 64 + 1, 256 * 128, 256 * 128 + 1, 256 * 199 + 77]
+    bt = build_batch(shape, [SeqSpec(i, L - 1, 1) for i, L in enumerate(lens)], seed=61,
+                     page_seed=62)
+    dd = to_device(bt, cfg)
+    _print_case("long rows combine", d, dtype)
+    out = run_decode(cfg, dd)
+    outp = run_prefill(cfg, to_device(bt, cfg))
+    assert_bitwise(outp, out, "decode (row-parallel combine) vs prefill (in-loop fold)")
+    rows = [(r, h) for r in range(len(lens)) for h in (0, 7)]
+    ref = oracle_rows(bt, rows)
+    got = np.stack([out[r, h].cpu().numpy() for r, h in rows])
+    assert_parity(got, ref, "long rows, sampled")
+    sl = dd.seq_lens.clone()
+    sl[1], sl[4] = 0, bt.max_seq_len + 1
+    o2 = torch.full_like(out, 0.0)
+    ws = torch.empty(bi.bi_attn_workspace_bytes(cfg, len(lens), bt.max_seq_len) // 4 + 64, device="cuda")
+    bi.bi_attn_decode(cfg, dd.q, dd.k_cache, dd.v_cache, dd.page_table, sl, bt.max_seq_len, o2, ws)
+    assert torch.isnan(o2[[1, 4]]).all()
+    good = [0, 2, 3, 5, 6]
+    assert_bitwise(o2[good], out[good], "valid long rows next to invalid ones")
+
+
 @pytest.mark.parametrize("seed", [2028, 3028])
 def test_long_decode_full_output(seed):
     """The long-context workload whole: 8 sequences of 131072 tokens, 64/4 heads, peaked softmax
