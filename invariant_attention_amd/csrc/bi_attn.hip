@@ -4,7 +4,10 @@
 //   page_update_kernel   scatter a step's new K/V rows into their pages (before attention)
 //   decode_split_kernel  one wave per (sequence, KV head, split): split partial -> workspace;
 //                        its APPEND form also writes each sequence's new token into its page
-//   combine_kernel       one wave per (token, q head): ascending fold of the partials, A / L
+//   combine_kernel       rows of at most 32 splits: one wave per 256 floats of a (token, KV
+//                        head)'s partials; ascending fold of the partials, A / L
+//   combine_rows_kernel  rows of more than 32 splits: one workgroup per (token, q head) row,
+//                        the row's reference, L and element chains in separate waves
 //   prefill_kernel       one workgroup per (sequence, KV head, query tile): every split of
 //                        every row in registers, folded in the loop, A / L in the epilogue
 // Both attention routes call subtile_step() and fold_scalars()/fold_elem() from core.hpp on
@@ -1443,9 +1446,11 @@ int launch_partials(const AttnParams& a, hipStream_t s) {
   return launch_partials_nb<E, D, 4, APPEND>(a, s);
 }
 
-// Lane width of the combine: up to 32 splits per row, four floats per lane and every split's
-// loads issued at once; beyond, one float per lane (four times the waves) and a 64-split ring,
-// so that a few long sequences still keep enough loads in flight.
+// Combine: up to 32 splits per row, one wave per 256 floats with four floats per lane and every
+// split's loads issued at once; beyond, one workgroup per row (combine_rows_kernel), whose
+// element waves address a row group's partials with 32-bit offsets. A row group too large for
+// those (2 GiB of partials) takes the one-wave kernel with one float per lane and a 64-split
+// ring instead, which gives the same bits.
 template <int D, int FPL, int U>
 void launch_combine_w(const AttnParams& a, hipStream_t s) {
   const int64_t waves = (int64_t)a.batch * a.hkv * ((a.group * D + 64 * FPL - 1) / (64 * FPL));
