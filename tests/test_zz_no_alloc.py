@@ -1,9 +1,10 @@
 """The allocation-free decode entry point (GPU): the same bits as bi_attn_decode.
 
 bi_attn_decode_noalloc keeps the split partials in the library's static device array instead
-of a caller workspace. Two calls in a row, the second with a smaller batch and shorter
-sequences (the array keeps the first call's partials, which the second must not read), both
-bitwise equal to bi_attn_decode with a NaN-poisoned workspace; a call needing more partials
+of a caller workspace. Calls in a row, each with a smaller batch or shorter sequences than the
+one before (the array keeps the earlier calls' partials, which the next must not read), the first
+with rows of more than 32 splits (the row-parallel combine), all bitwise equal to
+bi_attn_decode with a NaN-poisoned workspace; a call needing more partials
 than the array holds is refused before anything is launched.
 """
 
@@ -30,7 +31,7 @@ def _case(seed, B, lo, hi):
 
 
 def test_noalloc_decode_equals_decode_on_two_calls():
-    for seed, B, lo, hi in ((91, 48, 128, 8192), (92, 5, 1, 3000)):
+    for seed, B, lo, hi in ((90, 4, 9000, 20000), (91, 48, 128, 8192), (92, 5, 1, 3000)):
         cfg, bt = _case(seed, B, lo, hi)
         d = to_device(bt, cfg)
         ref = run_decode(cfg, d)                   # NaN-poisoned workspace
