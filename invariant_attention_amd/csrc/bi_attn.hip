@@ -633,8 +633,14 @@ __global__ __launch_bounds__(64 * (D / 64 + 2)) void combine_rows_kernel(AttnPar
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int G = a.group;
-  const int row = (int)blockIdx.x;                          // b Hq + h
-  if (row >= a.batch * a.hq) return;                        // (the whole workgroup)
+  // Workgroups go to the 8 XCDs in turn (workgroup i to XCD i % 8); the rows are dealt out so
+  // that XCD x takes the contiguous rows [x C, x C + C), C = ceil(rows / 8): the rows of one
+  // (sequence, KV head) share the 128-byte lines of their (m, l) pairs, which one L2 then fetches
+  // once. Workgroups past the last row exit.
+  const int nrows = a.batch * a.hq;
+  const int per_xcd = (nrows + 7) / 8;
+  const int row = (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);   // b Hq + h
+  if (row >= nrows) return;                                 // (the whole workgroup)
   const int rg = row / G, hl = row - rg * G, b = rg / a.hkv;
   const size_t blk0 = (size_t)rg * a.jmax * G;              // split 0 of the row group
   float* o = a.out + (size_t)row * D;
@@ -1461,7 +1467,7 @@ template <int D>
 void launch_combine_d(const AttnParams& a, hipStream_t s) {
   if (a.jmax <= 32) launch_combine_w<D, 4, 32>(a, s);
   else if ((int64_t)a.jmax * a.group * D * 4 < ((int64_t)1 << 31))
-    hipLaunchKernelGGL((combine_rows_kernel<D>), dim3((unsigned)(a.batch * a.hq)), dim3(64 * (D / 64 + 2)), 0, s, a);
+    hipLaunchKernelGGL((combine_rows_kernel<D>), dim3((unsigned)((a.batch * a.hq + 7) / 8 * 8)), dim3(64 * (D / 64 + 2)), 0, s, a);
   else launch_combine_w<D, 1, 64>(a, s);
 }
 int launch_combine(const AttnParams& a, int D, hipStream_t s) {
