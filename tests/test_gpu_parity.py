@@ -108,23 +108,24 @@ def test_split_edges_single_sequence():
         assert_bitwise(outp, torch.from_numpy(out), f"decode vs prefill L={L}")
 
 
-@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
-def test_long_rows_combine_windows(d, dtype):
+@pytest.mark.parametrize("d,dtype,hq,hkv", [(128, "bf16", 8, 2), (64, "f32", 8, 2), (64, "bf16", 2, 2)])
+def test_long_rows_combine_windows(d, dtype, hq, hkv):
     """Decode with rows of 1 to 200 splits in one call (the combine for rows of more than 32
     splits hands coefficients over in 64-split windows): windows that end exactly, one split
     past a window, a single split; every row bitwise equal to the prefill of the same token,
-    sampled rows against the oracle, and rows of invalid length NaN without touching the rest."""
-    shape = AttnShape(8, 2, d, 16, 256, dtype)
+    sampled rows against the oracle, and rows of invalid length NaN without touching the rest.
+    With 2 heads the 14 rows are not a multiple of the 8 XCDs the rows are dealt out to."""
+    shape = AttnShape(hq, hkv, d, 16, 256, dtype)
     cfg = cfg_for(shape)
     lens = [100, 256 * 63, 256 * 64, 256 * 64 + 1, 256 * 128, 256 * 128 + 1, 256 * 199 + 77]
     bt = build_batch(shape, [SeqSpec(i, L - 1, 1) for i, L in enumerate(lens)], seed=61,
                      page_seed=62)
     dd = to_device(bt, cfg)
-    _print_case("long rows combine", d, dtype)
+    _print_case("long rows combine", d, dtype, hq, hkv)
     out = run_decode(cfg, dd)
     outp = run_prefill(cfg, to_device(bt, cfg))
     assert_bitwise(outp, out, "decode (row-parallel combine) vs prefill (in-loop fold)")
-    rows = [(r, h) for r in range(len(lens)) for h in (0, 7)]
+    rows = [(r, h) for r in range(len(lens)) for h in (0, hq - 1)]
     ref = oracle_rows(bt, rows)
     got = np.stack([out[r, h].cpu().numpy() for r, h in rows])
     assert_parity(got, ref, "long rows, sampled")
