@@ -139,6 +139,28 @@ def test_long_rows_combine_windows(d, dtype, hq, hkv):
     assert_bitwise(o2[good], out[good], "valid long rows next to invalid ones")
 
 
+def test_decode_at_one_million_tokens():
+    """The largest decode here: one sequence of 2^20 tokens (4096 splits, 64 coefficient windows
+    in the long-row combine) beside one of 300001 tokens, decode_bf16 heads: sampled rows against
+    the oracle, every row bitwise equal to the prefill of the same token, and the shorter
+    sequence alone (other pages, a smaller max_seq_len) bitwise equal to its row of the pair."""
+    shape = CONFIG_SHAPES["decode_bf16"]
+    cfg = cfg_for(shape)
+    _print_case("decode at 2^20 tokens")
+    specs = [SeqSpec(0, (1 << 20) - 1, 1), SeqSpec(1, 300000, 1)]
+    bt = build_batch(shape, specs, seed=77, page_seed=78)
+    out = run_decode(cfg, to_device(bt, cfg))
+    rows = [(0, 0), (0, 31), (1, 5)]
+    got = np.stack([out[r, h].cpu().numpy() for r, h in rows])
+    assert_parity(got, oracle_rows(bt, rows), "decode at 2^20 tokens, sampled rows")
+    outp = run_prefill(cfg, to_device(bt, cfg))
+    assert_bitwise(outp, out, "decode vs prefill at 2^20 tokens")
+    del outp
+    alone = build_batch(shape, specs[1:], seed=77, page_seed=79)
+    out1 = run_decode(cfg, to_device(alone, cfg))
+    assert_bitwise(out1[0], out[1], "300001-token sequence alone vs beside the 2^20-token one")
+
+
 @pytest.mark.parametrize("seed", [2028, 3028])
 def test_long_decode_full_output(seed):
     """The long-context workload whole: 8 sequences of 131072 tokens, 64/4 heads, peaked softmax
