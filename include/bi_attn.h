@@ -118,6 +118,9 @@ size_t bi_attn_workspace_bytes(const bi_attn_cfg* cfg, int32_t rows_tokens, int3
  * bi_attn_prefill runs, so a token gets identical bits from either call.
  * workspace: device memory of at least bi_attn_workspace_bytes(cfg, batch, max_seq_len);
  * its contents are undefined on return. max_seq_len >= every seq_lens[b].
+ * Returns BI_EUNSUPPORTED, with nothing launched, when the partials of one (sequence, KV head)
+ * would reach 2 GiB: Jmax * (Hq / Hkv) * D * 4 >= 2^31 (Jmax below; at S = 256, Hq / Hkv = 16,
+ * D = 128 that is max_seq_len >= 2^26). Every decode entry point below shares this limit.
  */
 int bi_attn_decode(const bi_attn_cfg* cfg, const void* q, const void* k_cache,
                    const void* v_cache, const int32_t* page_table, int32_t max_pages,

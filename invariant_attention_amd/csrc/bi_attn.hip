@@ -509,23 +509,16 @@ __global__ __launch_bounds__((64 * DecWaves<E, NB>::value), 1) void decode_split
   }
 }
 
-// Combine. The partials of one (sequence, KV head) and split are a contiguous [group][D] block;
-// a wave owns 64 FPL consecutive floats of that block (lane: FPL floats of one row), folds them
-// over the splits in ascending j and writes A / L. The accumulator loads run U splits ahead of
-// the fold in a ring of U register slots (slot u holds split j with j % U == u; a slot is
-// refilled as soon as it is folded), the first few before the row's split count is known. Loads
+// Combine for rows of at most 32 splits. The partials of one (sequence, KV head) and split are a
+// contiguous [group][D] block; a wave owns 256 consecutive floats of that block (lane: four
+// floats of one row), folds them over the splits in ascending j and writes A / L. The
+// accumulator loads run U splits ahead of the fold in a ring of U register slots (slot u holds
+// split j with j % U == u; a slot is refilled as soon as it is folded), the first few before the
+// row's split count is known; every split's (m, l) pair is loaded with its accumulators. Loads
 // past the last split re-read it and are not folded, so every step issues the same loads.
-// With one float per lane a wave covers part of one row, and the (m, l) pairs of 64 splits
-// come in one load (lane i: split j0 + i), read out with readlane; with four floats per lane
-// every split's pairs are loaded with its accumulators.
-template <int FPL> struct CombVec;
-template <> struct CombVec<1> { typedef float T; };
-template <> struct CombVec<4> { typedef f32x4 T; };
-template <int D, int FPL, int U>
+template <int D, int U>
 __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
-  using V = typename CombVec<FPL>::T;
-  constexpr bool WIN = FPL == 1;   // (m, l) in 64-split windows (one window per ring turn)
-  static_assert(!WIN || U == 64, "one (m, l) window per ring turn");
+  constexpr int FPL = 4;
   const int lane = threadIdx.x & 63;
   const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
   const int G = a.group;
@@ -542,28 +535,24 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
   const float* acc = a.ws_acc + blk0 * D + f;
   const size_t ml_step = G, acc_step = (size_t)G * D;
   const int seq_len = a.seq_lens[b];
-  float2 mlj[WIN ? 1 : U], mlw = {0.f, 0.f}, mlw_next = {0.f, 0.f};
-  V accj[U];
+  float2 mlj[U];
+  f32x4 accj[U];
   // the first kEarly loads go out with the length's; the rest of the ring once the row's split
   // count J is known (clamped to its last split, so no load reads another row's slots)
   constexpr int kEarly = 4;
 #pragma unroll
   for (int u = 0; u < kEarly; ++u) {
     const int jj = min(u, a.jmax - 1);
-    if (!WIN) mlj[u] = ml[jj * ml_step];
-    accj[u] = *(const V*)(acc + jj * acc_step);
+    mlj[u] = ml[jj * ml_step];
+    accj[u] = *(const f32x4*)(acc + jj * acc_step);
   }
   const bool bad = seq_len <= 0 || seq_len > a.max_seq_len;
   const int J = bad ? 1 : (seq_len - 1) / split_len(a, seq_len) + 1;
-  if (WIN) {
-    mlw = ml[min(lane, J - 1) * ml_step];
-    mlw_next = ml[min(64 + lane, J - 1) * ml_step];
-  }
 #pragma unroll
   for (int u = kEarly; u < U; ++u) {
     const int jj = min(u, J - 1);
-    if (!WIN) mlj[u] = ml[jj * ml_step];
-    accj[u] = *(const V*)(acc + jj * acc_step);
+    mlj[u] = ml[jj * ml_step];
+    accj[u] = *(const f32x4*)(acc + jj * acc_step);
   }
   if (bad) {
 #pragma unroll
@@ -575,45 +564,24 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnParams a) {
 #pragma unroll
   for (int e = 0; e < FPL; ++e) A[e] = 0.f;
   for (int j0 = 0; j0 < J; j0 += U) {
-    float2 mw = mlw;
-    if (WIN && j0 > 0) {
-      mw = mlw_next;
-      mlw_next = ml[min(j0 + 64 + lane, J - 1) * ml_step];
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < J) {
-        float m, l;
-        if (WIN) {
-          m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mw.x), u));
-          l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mw.y), u));
-        } else {
-          m = mlj[WIN ? 0 : u].x;
-          l = mlj[WIN ? 0 : u].y;
-        }
         float fa, fb;
-        fold_scalars(M, L, m, l, fa, fb);
-        const V x = accj[u];
+        fold_scalars(M, L, mlj[u].x, mlj[u].y, fa, fb);
+        const f32x4 x = accj[u];
 #pragma unroll
-        for (int e = 0; e < FPL; ++e) {
-          float xe;
-          if constexpr (FPL == 1) xe = x;
-          else xe = x[e];
-          A[e] = fold_elem(A[e], xe, fa, fb);
-        }
+        for (int e = 0; e < FPL; ++e) A[e] = fold_elem(A[e], x[e], fa, fb);
       }
       const int jn = min(j0 + u + U, J - 1);
-      if (!WIN) mlj[u] = ml[jn * ml_step];
-      accj[u] = *(const V*)(acc + jn * acc_step);
+      mlj[u] = ml[jn * ml_step];
+      accj[u] = *(const f32x4*)(acc + jn * acc_step);
     }
   }
-  V r;
-  if constexpr (FPL == 1) r = A[0] / L;
-  else {
+  f32x4 r;
 #pragma unroll
-    for (int e = 0; e < FPL; ++e) r[e] = A[e] / L;
-  }
-  *(V*)o = r;
+  for (int e = 0; e < FPL; ++e) r[e] = A[e] / L;
+  *(f32x4*)o = r;
 }
 
 // Combine for long rows (more than 32 splits). The fold of a row is one sequential chain per
@@ -1454,21 +1422,17 @@ int launch_partials(const AttnParams& a, hipStream_t s) {
 
 // Combine: up to 32 splits per row, one wave per 256 floats with four floats per lane and every
 // split's loads issued at once; beyond, one workgroup per row (combine_rows_kernel), whose
-// element waves address a row group's partials with 32-bit offsets. A row group too large for
-// those (2 GiB of partials) takes the one-wave kernel with one float per lane and a 64-split
-// ring instead, which gives the same bits.
-template <int D, int FPL, int U>
-void launch_combine_w(const AttnParams& a, hipStream_t s) {
-  const int64_t waves = (int64_t)a.batch * a.hkv * ((a.group * D + 64 * FPL - 1) / (64 * FPL));
-  const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
-  hipLaunchKernelGGL((combine_kernel<D, FPL, U>), grid, dim3(kThreads), 0, s, a);
-}
+// element waves address a row group's partials with 32-bit offsets (decode_params refuses a call
+// whose row group would pass 2 GiB of partials).
 template <int D>
 void launch_combine_d(const AttnParams& a, hipStream_t s) {
-  if (a.jmax <= 32) launch_combine_w<D, 4, 32>(a, s);
-  else if ((int64_t)a.jmax * a.group * D * 4 < ((int64_t)1 << 31))
+  if (a.jmax <= 32) {
+    const int64_t waves = (int64_t)a.batch * a.hkv * ((a.group * D + 255) / 256);
+    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+    hipLaunchKernelGGL((combine_kernel<D, 32>), grid, dim3(kThreads), 0, s, a);
+  } else {
     hipLaunchKernelGGL((combine_rows_kernel<D>), dim3((unsigned)((a.batch * a.hq + 7) / 8 * 8)), dim3(64 * (D / 64 + 2)), 0, s, a);
-  else launch_combine_w<D, 1, 64>(a, s);
+  }
 }
 int launch_combine(const AttnParams& a, int D, hipStream_t s) {
   if (D == 128) launch_combine_d<128>(a, s);
@@ -1491,6 +1455,10 @@ int decode_params(const bi_attn_cfg* cfg, const void* q, const void* k_cache, co
     return BI_EINVAL;
   if (need_kv && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))) return BI_EINVAL;
   if (need_out && (!out || !aligned16(out))) return BI_EINVAL;
+  // the row-parallel combine addresses one (sequence, KV head)'s partials with 32-bit offsets
+  if (jmax_of(cfg, batch, max_seq_len) * (cfg->num_q_heads / cfg->num_kv_heads) * cfg->head_dim * 4 >=
+      ((int64_t)1 << 31))
+    return BI_EUNSUPPORTED;
   const size_t need = ws_bytes(cfg, batch, batch, max_seq_len);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return BI_EWORKSPACE;
   *a = base_params(cfg);

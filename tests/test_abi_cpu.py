@@ -97,6 +97,13 @@ def test_argument_validation_launches_nothing():
     assert need > 0
     assert lib.bi_attn_decode(ctypes.byref(c), f, f, f, f, 4, 4, f, 1, 16, f, None, 0, None) == E.BI_EWORKSPACE
     assert lib.bi_attn_decode(ctypes.byref(c), f, f, f, f, 4, 4, f, 1, 16, f, f, need - 1, None) == E.BI_EWORKSPACE
+    # partials of one (sequence, KV head) reaching 2 GiB: refused before the workspace check
+    G, D = BASE["num_q_heads"] // BASE["num_kv_heads"], BASE["head_dim"]
+    lim = (1 << 31) // (G * D * 4) * BASE["split_size"]   # first max_seq_len refused
+    assert lib.bi_attn_decode(ctypes.byref(c), f, f, f, f, 4, 4, f, 1, lim, f, None, 0, None) == E.BI_EUNSUPPORTED
+    assert lib.bi_attn_decode_combine(ctypes.byref(c), f, 1, lim, f, None, 0, None) == E.BI_EUNSUPPORTED
+    assert lib.bi_attn_decode(ctypes.byref(c), f, f, f, f, 4, 4, f, 1, lim - BASE["split_size"], f, None, 0,
+                              None) == E.BI_EWORKSPACE
     # empty work is a no-op success
     assert lib.bi_attn_decode(ctypes.byref(c), None, None, None, None, 0, 0, None, 0, 0, None, None, 0, None) == E.BI_OK
     assert lib.bi_attn_prefill(ctypes.byref(c), None, None, None, None, 0, 0, None, None, 0, 0, 0, 0, None, None, 0, None) == E.BI_OK
